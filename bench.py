@@ -1,0 +1,257 @@
+"""Benchmark of one Veda attention layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload headline] [--no-cpu]
+
+A step is the whole hot path over the layer: plan (tile packing), select
+(pooling, fp64 tile logits, top-k -> CSR tile lists) and attend (tile-skip
+attention), with q/k/v already resident in HBM. Timing uses HIP events on the
+stream the kernels run on. Prints one JSON line:
+  value        kept-tile TFLOP/s of the whole step (kept pairs x 4*128^2*D / step time)
+  ms_per_step  ms per layer (plan + select + attend)
+  roofline     the attend kernel against MI355X's dense bf16 MFMA peak
+  cpu_baseline the CPU oracle on a bounded sample of the same layer, scaled
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "kept-tile attention TFLOP/s & ms/layer at 104k tokens, 90% sparse; % MFMA peak"
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense bf16 MFMA)
+HBM_PEAK_GBS = 8000.0
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Device buffers and the three stage calls for one workload."""
+
+    def __init__(self, inp):
+        import torch
+        import learned_block_sparse_amd as veda
+        import workloads
+        self.veda = veda
+        wl = inp.workload
+        self.wl = wl
+        dev = torch.device("cuda", 0)
+        self.t = {}
+        for name in ("q", "k", "v"):
+            x = getattr(inp, name)
+            if wl.dtype == "bf16":
+                t = torch.from_numpy(workloads.bf16_bits(x).view(np.int16)).view(torch.bfloat16)
+            else:
+                t = torch.from_numpy(x)
+            self.t[name] = t.to(dev)
+        self.out = torch.empty_like(self.t["q"])
+        pq = torch.from_numpy(inp.proj_q).to(dev)
+        pk = torch.from_numpy(inp.proj_k).to(dev)
+        gen, ref = veda.budget(wl.generated), veda.budget(wl.reference)
+        tile_refs = not (ref.tiles < 0 and ref.ratio >= 1.0)
+        groups = {}
+        for h, s in enumerate(wl.head_shapes):
+            groups.setdefault(s, []).append(h)
+        self.groups = []
+        for shape, heads in groups.items():
+            spans = [(s, g, None) for s, g in wl.refs] if tile_refs else []
+            spans.append((wl.target[0], wl.target[1], shape))
+            info = veda.veda_plan_query(spans, wl.seq_len)
+            sel = veda.veda_select_query(info, gen, ref, wl.head_dim, len(heads))
+            idx = torch.tensor(heads, dtype=torch.long, device=dev)
+            g = dict(info=info, sel=sel, heads=heads,
+                     perm=torch.empty(info.n_slots, dtype=torch.int32, device=dev),
+                     vc=torch.empty(info.n_tiles, dtype=torch.int32, device=dev),
+                     ro=torch.empty(info.n_tiles + 1, dtype=torch.int32, device=dev),
+                     cols=torch.empty(len(heads) * sel.entries_per_head, dtype=torch.int32, device=dev),
+                     ws=torch.empty(sel.workspace_bytes, dtype=torch.uint8, device=dev),
+                     pq=pq.index_select(0, idx).contiguous(), pk=pk.index_select(0, idx).contiguous())
+            self.groups.append(g)
+        self.pairs = sum(len(g["heads"]) * g["sel"].entries_per_head for g in self.groups)
+        self.flops = self.pairs * 4.0 * 128 * 128 * wl.head_dim
+
+    def plan(self):
+        for g in self.groups:
+            self.veda.veda_plan(g["info"], g["perm"], g["vc"])
+
+    def select(self):
+        v = self.veda
+        for g in self.groups:
+            v.veda_select(g["info"], g["sel"], g["perm"], g["vc"], self.t["q"], self.t["k"],
+                          g["heads"], g["pq"], g["pk"], row_offsets=g["ro"], cols=g["cols"],
+                          workspace=g["ws"])
+
+    def attend(self):
+        v = self.veda
+        for g in self.groups:
+            v.veda_attend(g["info"], g["sel"], g["perm"], g["vc"], self.t["q"], self.t["k"],
+                          self.t["v"], g["heads"], g["ro"], g["cols"], out=self.out)
+
+
+def _cpu_baseline(inp, layer_pairs, head_dim, seconds):
+    """The oracle, as it stands, on a bounded sample of the same layer: pool,
+    logits and selection for head 0 (one of H), then exact attention for
+    query tiles of head 0 in a seeded order until `seconds` have passed.
+    The whole layer's time is extrapolated as H x (head-0 selection) +
+    (kept pairs of the layer / kept pairs attended) x (attention time)."""
+    from oracle import attention, layer as olayer, selection
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001 - report what can be known
+        threads = len(os.sched_getaffinity(0))
+    wl = inp.workload
+    shape = wl.head_shapes[0]
+    from oracle import budget as obudget, predictor, tiles as otiles
+    gen, ref = obudget.from_request(wl.generated), obudget.from_request(wl.reference)
+    t0 = time.perf_counter()
+    oshape = otiles.least_padding_shape(wl.target[1]) if shape is None else shape
+    lay = olayer.layout_for(wl, oshape, gen, ref)
+    t_plan = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    blocks = selection.column_blocks(lay, gen, ref)
+    fq = predictor.pool(inp.q, lay, [0])
+    fk = predictor.pool(inp.k, lay, [0])
+    sc = predictor.logits(fq, fk, inp.proj_q[[0]], inp.proj_k[[0]])
+    kept = selection.select(sc, lay, blocks)
+    mask = selection.block_mask(kept, lay)
+    t_sel = time.perf_counter() - t0
+    order = np.random.default_rng(99).permutation(lay.n_tiles)
+    done_pairs, t_att, n_tiles = 0, 0.0, 0
+    for a in order:
+        t0 = time.perf_counter()
+        attention.attend(inp.q, inp.k, inp.v, lay, mask, [0], query_tiles=[a])
+        t_att += time.perf_counter() - t0
+        done_pairs += int(mask[0, a].sum())
+        n_tiles += 1
+        if t_att + t_sel >= seconds:
+            break
+    est = t_plan + wl.n_heads * t_sel + t_att * (layer_pairs / max(1, done_pairs))
+    flops = layer_pairs * 4.0 * 128 * 128 * head_dim
+    return {
+        "value": flops / est / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"head 0 of {wl.n_heads}: plan + pool + logits + select ({t_sel:.2f} s), then "
+                   f"exact fp64 attention for {n_tiles} query tiles ({done_pairs} kept pairs, "
+                   f"{t_att:.2f} s); layer time extrapolated to {est:.1f} s"),
+        "est_layer_s": est,
+    }
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the Veda hot path is single-GPU "
+              f"(heads would shard with no exchange); got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+
+    torch.cuda.set_device(0)
+    _log(f"[bench] generating {args.workload}")
+    inp = workloads.generate(args.workload)
+    wl = inp.workload
+    L = Layer(inp)
+    _log(f"[bench] kept pairs {L.pairs}, {L.flops / 1e12:.3f} TFLOP per layer")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    # cold plan (first call)
+    e0, e1 = ev(), ev()
+    e0.record()
+    L.plan()
+    e1.record()
+    torch.cuda.synchronize()
+    plan_cold_ms = e0.elapsed_time(e1)
+
+    for _ in range(args.warmup):
+        L.plan(); L.select(); L.attend()
+    torch.cuda.synchronize()
+    _log("[bench] warmup done")
+
+    marks = []
+    t_start, t_stop = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        m = [ev() for _ in range(4)]
+        m[0].record(); L.plan()
+        m[1].record(); L.select()
+        m[2].record(); L.attend()
+        m[3].record()
+        marks.append(m)
+    t_stop.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_step = total_ms / args.steps
+    plan_ms = [m[0].elapsed_time(m[1]) for m in marks]
+    sel_ms = [m[1].elapsed_time(m[2]) for m in marks]
+    att_ms = [m[2].elapsed_time(m[3]) for m in marks]
+    att_avg = float(np.mean(att_ms))
+    _log(f"[bench] step {ms_step:.3f} ms: plan {np.median(plan_ms):.3f} select "
+         f"{np.median(sel_ms):.3f} attend {np.median(att_ms):.3f}")
+
+    attend_tflops = L.flops / (att_avg * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": L.flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.note}",
+            "seq_len": wl.seq_len, "heads": wl.n_heads, "head_dim": wl.head_dim,
+            "generated_budget": list(wl.generated), "reference_budget": list(wl.reference),
+            "kept_tile_pairs": L.pairs, "tflop_per_layer": L.flops / 1e12,
+            "parallelism": "single GPU",
+        },
+        "stages_ms": {
+            "plan_cold": plan_cold_ms,
+            "plan_median": float(np.median(plan_ms)),
+            "select_median": float(np.median(sel_ms)),
+            "attend_median": float(np.median(att_ms)),
+            "attend_p10": float(np.percentile(att_ms, 10)),
+            "attend_p90": float(np.percentile(att_ms, 90)),
+        },
+        "attend_tflops": attend_tflops,
+        "attend_pct_bf16_peak": 100.0 * attend_tflops / BF16_PEAK_TFLOPS,
+        "roofline": {
+            "bound": "mfma", "achieved": attend_tflops, "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": attend_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        _log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = _cpu_baseline(inp, L.pairs, wl.head_dim, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

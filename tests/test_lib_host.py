@@ -1,0 +1,162 @@
+"""libveda on the CPU: the library loads, exports every entry point its header
+declares, and its host-side logic (span validation, least-padding boxes,
+layout sizes, budget splits with Python's rounding, CSR sizing) agrees with
+the oracle. No kernel is launched here."""
+import math
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import learned_block_sparse_amd as veda
+from learned_block_sparse_amd import _lib
+from oracle import tiles, budget, selection, layer
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    header = open(os.path.join(ROOT, "include", "veda.h")).read()
+    declared = set(re.findall(r"\b(veda_[a-z_]+)\s*\(", header))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert "gfx950" in veda.version()
+
+
+def _spans(wl, shape, tile_refs=True):
+    sp = [(s, g, None) for s, g in wl.refs] if tile_refs else []
+    sp.append((wl.target[0], wl.target[1], shape))
+    return sp
+
+
+@pytest.mark.parametrize("name", ["tiny", "padding", "mid", "headline", "long"])
+def test_plan_query_matches_oracle_layout(name):
+    wl = workloads.get(name)
+    for shape in sorted(set(wl.head_shapes), key=str):
+        info = veda.veda_plan_query(_spans(wl, shape), wl.seq_len)
+        oshape = tiles.least_padding_shape(wl.target[1]) if shape is None else shape
+        ospans = [(s, g, tiles.least_padding_shape(g)) for s, g in wl.refs]
+        ospans.append((wl.target[0], wl.target[1], oshape))
+        lay = tiles.build_layout(ospans, wl.seq_len)
+        assert (info.n_tiles, info.n_video, info.n_ref, info.n_global) == \
+            (lay.n_tiles, lay.n_video, lay.n_ref, lay.n_global)
+        assert info.n_slots == lay.n_slots
+        assert (info.ref_tokens, info.target_tokens) == (lay.ref_tokens, lay.target_tokens)
+        for i, (_, _, s) in enumerate(ospans):
+            assert tuple(info.spans[i].shape) == tuple(s)
+
+
+@pytest.mark.parametrize("grid", [(5, 12, 20), (31, 48, 70), (1, 48, 84), (61, 45, 80),
+                                  (1, 1, 1), (3, 200, 7), (130, 1, 1), (2, 2, 2)])
+def test_least_padding_choice_matches_oracle(grid):
+    info = veda.veda_plan_query([(0, grid, None)], grid[0] * grid[1] * grid[2])
+    assert tuple(info.spans[0].shape) == tiles.least_padding_shape(grid)
+
+
+@pytest.mark.parametrize("spans,seq", [
+    ([], 10),
+    ([(0, (1, 8, 8), (1, 8, 16)), (32, (1, 8, 8), (1, 8, 16))], 200),
+    ([(0, (1, 8, 8), (1, 8, 16))], 63),
+    ([(-1, (1, 8, 8), (1, 8, 16))], 100),
+    ([(0, (1, 8, 8), (1, 8, 8))], 100),          # not a 128-cell box
+    ([(0, (0, 8, 8), None)], 100),               # empty grid
+])
+def test_plan_query_refuses_like_the_oracle(spans, seq):
+    with pytest.raises(veda.VedaError):
+        veda.veda_plan_query(spans, seq)
+    ospans = [(s, g, sh if sh is not None else (1, 8, 16)) for s, g, sh in spans]
+    if all(sh is None or sh[0] * sh[1] * sh[2] == 128 for _, _, sh in spans) and \
+            all(min(g) > 0 for _, g, _ in spans):
+        with pytest.raises(tiles.VedaError):
+            tiles.build_layout(ospans, seq)
+
+
+@pytest.mark.parametrize("name", ["tiny", "padding", "mid", "headline", "long"])
+def test_select_query_matches_oracle_blocks_and_sizes(name):
+    wl = workloads.get(name)
+    gen, ref = budget.from_request(wl.generated), budget.from_request(wl.reference)
+    for shape in sorted(set(wl.head_shapes), key=str):
+        info = veda.veda_plan_query(_spans(wl, shape), wl.seq_len)
+        sel = veda.veda_select_query(info, veda.budget(wl.generated), veda.budget(wl.reference),
+                                     wl.head_dim, wl.n_heads)
+        oshape = tiles.least_padding_shape(wl.target[1]) if shape is None else shape
+        lay = layer.layout_for(wl, oshape, gen, ref)
+        blocks = selection.column_blocks(lay, gen, ref)
+        params = selection.block_params(lay, blocks)
+        assert sel.n_blocks == len(params)
+        for b, (start, stop, keep_all, lo, hi, frac) in enumerate(params):
+            k = sel.blocks[b]
+            assert (k.start, k.stop, bool(k.keep_all), k.k_lo, k.k_hi) == (start, stop, keep_all, lo, hi)
+            assert k.frac == frac                      # bit-identical double
+        # CSR size: closed form per row, summed
+        nv = lay.n_video
+        want = sum(nv * lo + math.floor(nv * frac) for (_, _, _, lo, _, frac) in params)
+        want += nv * lay.n_global + lay.n_global * lay.n_tiles
+        assert sel.entries_per_head == want
+
+
+@pytest.mark.parametrize("name", ["tiny", "padding", "mid"])
+def test_select_query_entries_equal_oracle_mask(name):
+    inp = workloads.generate(name)
+    wl = inp.workload
+    groups, _ = layer.run(inp, do_attend=False)
+    for g in groups:
+        info = veda.veda_plan_query(_spans(wl, g.shape), wl.seq_len)
+        sel = veda.veda_select_query(info, veda.budget(wl.generated), veda.budget(wl.reference),
+                                     wl.head_dim, len(g.heads))
+        per_head = g.mask.sum(axis=(1, 2))
+        assert (per_head == sel.entries_per_head).all()
+        assert sel.widest == g.mask.sum(axis=2).max()
+
+
+def test_budget_split_matches_python_rounding():
+    """Tile budgets b over n columns give frac = round(b - floor(b), 12):
+    libveda's decimal rounding (printf + strtod) against Python's round()."""
+    rng = random.Random(1234)
+    info = veda.veda_plan_query([(0, (1, 8, 16 * 4000), (1, 8, 16))], 128 * 4000)
+    n = info.n_video
+    mism = 0
+    for i in range(30000):
+        b = rng.uniform(1.0, n - 1.0) if i % 3 else rng.randint(1, n - 2) + rng.random() * 1e-9
+        sel = veda.veda_select_query(info, veda.budget(("tiles", b)), veda.budget(("tiles", b)), 64, 1)
+        lo, hi, frac = budget.split(b, n)
+        k = sel.blocks[0]
+        mism += (k.k_lo, k.k_hi, k.frac) != (lo, hi, frac)
+    assert mism == 0
+
+
+def test_ratio_budget_matches_python_arithmetic():
+    rng = random.Random(99)
+    for _ in range(3000):
+        T, H, W = rng.randint(1, 40), rng.randint(1, 60), rng.randint(1, 90)
+        seq = T * H * W + rng.randint(0, 300)
+        ratio = rng.random() * 1.1
+        info = veda.veda_plan_query([(0, (T, H, W), None)], seq)
+        sel = veda.veda_select_query(info, veda.budget(("ratio", ratio)),
+                                     veda.budget(("ratio", ratio)), 128, 1)
+        n = info.n_video
+        bud = (ratio, None)
+        k = sel.blocks[0]
+        if budget.keeps_all(bud):
+            assert k.keep_all == 1
+            continue
+        want = budget.split(budget.per_row(bud, T * H * W, n), n)
+        assert (k.k_lo, k.k_hi, k.frac) == want
+
+
+@pytest.mark.parametrize("bad", [("ratio", -0.5), ("tiles", -1.0)])
+def test_select_query_refuses_bad_budget(bad):
+    info = veda.veda_plan_query([(0, (4, 16, 16), None)], 1024)
+    with pytest.raises(veda.VedaError):
+        veda.veda_select_query(info, veda.budget(bad), veda.budget(bad), 64, 1)
+
+
+def test_select_query_unsupported_head_dim():
+    info = veda.veda_plan_query([(0, (4, 16, 16), None)], 1024)
+    with pytest.raises(veda.VedaUnsupported):
+        veda.veda_select_query(info, veda.budget(("ratio", 0.2)), veda.budget(("ratio", 0.2)), 96, 1)
