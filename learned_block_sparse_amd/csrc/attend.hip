@@ -5,16 +5,12 @@
 // plan's permutation and writing each real query row's output straight to
 // its original row (no tile-ordered copies, no scatter pass).
 //
-// bf16 kernel (MFMA, gfx950):
-//   4 wavefronts x 32 query rows. Per kept key tile, K (128 x D) and V are
-//   staged in LDS. Scores are formed transposed, S^T = K Q^T, with
-//   v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the wave's Q held
-//   in registers as B), so each lane holds 64 scores of ONE query row: the
+// bf16 kernel (MFMA, gfx950): scores are formed transposed, S^T = K Q^T,
+//   with v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the wave's Q
+//   held in registers as B), so each lane holds the scores of ONE query row:
 //   row max and row sum are in-lane reductions plus one exchange with the
-//   lane 32 apart. The probabilities, converted to bf16, are already laid
-//   out as the B operand of O^T += V^T P^T; V is stored transposed in LDS
-//   with keys permuted inside each 16-key group ({0-3, 8-11 | 4-7, 12-15})
-//   so that each A operand is one 16-byte LDS read.
+//   lane 32 apart, and the probabilities, converted to bf16, are already laid
+//   out as the B operand of O^T += V^T P^T. Details at the kernel.
 // f32 kernel (vector ALU): 2 threads per query row, keys in chunks of 32.
 #include "kernels.hpp"
 
@@ -64,23 +60,65 @@ __host__ inline uint32_t grid_blocks(const AttendArgs &a) {
 }
 
 // --------------------------------------------------------------- bf16 MFMA --
+// 8 wavefronts (2 per SIMD): wave w takes query rows 32*(w%4) .. +31 and key
+// half w/4 (keys 64*(w/4) .. +63) of every kept tile, with its own online
+// softmax state; the two halves are merged through LDS at the end. Two
+// waves per SIMD let one wave's softmax (VALU) run while the other's MFMAs
+// execute.
+//
+// K and V tiles are double-buffered in LDS, row-major, each 16-byte chunk c of
+// row r stored at chunk position c ^ swz(r) so that both access patterns are
+// free of bank conflicts:
+//   K: the A operand of S^T = K Q^T, one 16-byte read of 8 d-values per lane
+//      for 32 consecutive rows;
+//   V: the A operand of O^T += V^T P^T, built by ds_read_b64_tr_b16. Within a
+//      16-lane group that instruction hands lane i, element j, the (i%4)-th
+//      16-bit value of the 8 bytes addressed by lane i/4 + 4j; with source
+//      lane s pointing at row (key) k0 + s/4, columns d0 + 4*(s%4), lane i
+//      receives V[k0 + j][d0 + i] for j = 0..3: four keys of one column.
+// Tiles are staged through registers: the loads of tile t+2's rows are
+// issued while tile t is computed and written to the free buffer one
+// iteration later, so no wave waits on a global load it just issued. The
+// row ids (perm) are fetched one tile further ahead, one per lane, and
+// broadcast within the wave by shuffles.
 template <int D>
 struct Bf16Cfg {
-  static constexpr int KPITCH = D * 2 + 16;        // bytes per K row in LDS
-  static constexpr int VPITCH = VEDA_TILE * 2 + 16;  // bytes per V^T row (one d)
-  static constexpr int K_UNITS = VEDA_TILE * D / 8 / 256;  // 16-byte K loads per thread
-  static constexpr int V_UNITS = 32 * (D / 8) / 256;       // 4-row V groups per thread
-  static constexpr int LDS_BYTES = VEDA_TILE * KPITCH + D * VPITCH;
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CHUNKS = D / 8;                        // 16-byte chunks per row
+  static constexpr int TILE_BYTES = VEDA_TILE * ROW_BYTES;
+  static constexpr int BUF_BYTES = 2 * TILE_BYTES;            // K then V
+  static constexpr int LDS_BYTES = 2 * BUF_BYTES;             // double-buffered
+  static constexpr int ROWS_PER_LOAD = 64 / CHUNKS;           // rows one 64-lane load covers
+  static constexpr int LOADS = 16 / ROWS_PER_LOAD;            // loads per wave per tensor
+  static constexpr int DB = D / 32;                           // 32-wide d blocks of O^T
 };
+
+template <int D>
+__device__ inline int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ inline int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
 
 __device__ inline uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// Rows of padding slots read zeros from here, as the page's tile-ordered
+// copies hold zeros in padding slots.
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[128] = {};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ inline s16x4 ds_read_tr(const unsigned char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+}
+
 template <int D>
-__global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadList heads) {
+__global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadList heads) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
-  unsigned char *k_lds = lds;
-  unsigned char *v_lds = lds + VEDA_TILE * C::KPITCH;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const BlockMap bm = map_block(a, blockIdx.x);
   if (!bm.live) return;
@@ -93,10 +131,11 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
   const int g = lane / 32, l32 = lane % 32;
+  const int qg = wave & 3, kh = wave >> 2;
 
-  // Q fragment (B operand of S^T = K Q^T): lane holds q[row][16*ks + 8*g .. +8].
+  // Q fragment (B operand of S^T = K Q^T): q[row][16*ks + 8*g .. +8]
   const int32_t vc_q = a.valid_count[tile];
-  const int qi = wave * 32 + l32;
+  const int qi = qg * 32 + l32;
   const int32_t qrow = qi < vc_q ? a.perm[int64_t(tile) * VEDA_TILE + qi] : -1;
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -106,158 +145,184 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
     qf[ks] = __builtin_bit_cast(bf16x8, u);
   }
 
-  f32x16 o[D / 32];
+  f32x16 o[C::DB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int32_t t_begin = a.row_offsets[tile], t_end = a.row_offsets[tile + 1];
   const int32_t *list = a.cols + int64_t(hi) * a.entries_per_head;
+  const int n_t = t_end - t_begin;
 
-  uint4 kreg[C::K_UNITS];
-  uint4 vreg[C::V_UNITS][4];
-  auto load_tile = [&](int32_t j) {
-    const int32_t vc = a.valid_count[j];
-    const int32_t *pj = a.perm + int64_t(j) * VEDA_TILE;
+  // Row ids: lane holds perm[j*128 + 16*wave + lane%16] of a tile j.
+  auto fetch_rows = [&](int idx) -> int32_t {
+    if (idx >= n_t) return -1;
+    const int32_t j = list[t_begin + idx];
+    return a.perm[int64_t(j) * VEDA_TILE + 16 * wave + (lane & 15)];
+  };
+  uint4 kreg[C::LOADS], vreg[C::LOADS];
+  auto issue_loads = [&](int32_t rows) {
 #pragma unroll
-    for (int it = 0; it < C::K_UNITS; ++it) {
-      const int u = tid + 256 * it;
-      const int key = u / (D / 8), dc = u % (D / 8);
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (key < vc) x = ld16(kb_ + int64_t(pj[key]) * a.stride_s + dc * 8);
-      kreg[it] = x;
-    }
-#pragma unroll
-    for (int it = 0; it < C::V_UNITS; ++it) {
-      const int u = tid + 256 * it;
-      const int c = u % 32, dc = u / 32;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = 4 * c + rr;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (key < vc) x = ld16(vb + int64_t(pj[key]) * a.stride_s + dc * 8);
-        vreg[it][rr] = x;
-      }
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int r = C::ROWS_PER_LOAD * i + lane / C::CHUNKS;   // row within the wave's 16
+      const int c = lane % C::CHUNKS;
+      const int32_t rid = __shfl(rows, r, 64);
+      const uint16_t *ks = rid >= 0 ? kb_ + int64_t(rid) * a.stride_s + c * 8 : g_zero_row + c * 8;
+      const uint16_t *vs = rid >= 0 ? vb + int64_t(rid) * a.stride_s + c * 8 : g_zero_row + c * 8;
+      kreg[i] = ld16(ks);
+      vreg[i] = ld16(vs);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    unsigned char *kd = lds + buf * C::BUF_BYTES;
+    unsigned char *vd = kd + C::TILE_BYTES;
 #pragma unroll
-    for (int it = 0; it < C::K_UNITS; ++it) {
-      const int u = tid + 256 * it;
-      const int key = u / (D / 8), dc = u % (D / 8);
-      *reinterpret_cast<uint4 *>(k_lds + key * C::KPITCH + dc * 16) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < C::V_UNITS; ++it) {
-      const int u = tid + 256 * it;
-      const int c = u % 32, dc = u / 32;
-      // keys 4c..4c+3 go to position (16*(c/4) + 4*blk) with blk = {0,2,1,3}[c%4]
-      const int cq = c % 4;
-      const int posblk = (cq == 1) ? 2 : (cq == 2) ? 1 : cq;
-      const int col = 16 * (c / 4) + 4 * posblk;
-      const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&vreg[it][0]);
-      const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&vreg[it][1]);
-      const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&vreg[it][2]);
-      const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&vreg[it][3]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // d = 8*dc + 2w (low halves) and 8*dc + 2w + 1 (high halves)
-        uint2 lo, hi2;
-        lo.x = (r0[w] & 0xffffu) | (r1[w] << 16);
-        lo.y = (r2[w] & 0xffffu) | (r3[w] << 16);
-        hi2.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-        hi2.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-        const int d0 = 8 * dc + 2 * w;
-        *reinterpret_cast<uint2 *>(v_lds + d0 * C::VPITCH + col * 2) = lo;
-        *reinterpret_cast<uint2 *>(v_lds + (d0 + 1) * C::VPITCH + col * 2) = hi2;
-      }
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int row = 16 * wave + C::ROWS_PER_LOAD * i + lane / C::CHUNKS;
+      const int c = lane % C::CHUNKS;
+      *reinterpret_cast<uint4 *>(kd + row * C::ROW_BYTES + ((c ^ swz_k<D>(row)) << 4)) = kreg[i];
+      *reinterpret_cast<uint4 *>(vd + row * C::ROW_BYTES + ((c ^ swz_v<D>(row)) << 4)) = vreg[i];
     }
   };
 
-  if (t_begin < t_end) load_tile(list[t_begin]);
-  for (int32_t t = t_begin; t < t_end; ++t) {
-    const int32_t vcj = a.valid_count[list[t]];
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < t_end) load_tile(list[t + 1]);
+  // prologue: tile 0 staged into buffer 0, tile 1's loads in flight
+  int32_t rows_next = fetch_rows(0);
+  issue_loads(rows_next);
+  rows_next = fetch_rows(1);
+  store_tile(0);
+  int32_t rows_after = fetch_rows(2);
+  if (n_t > 1) issue_loads(rows_next);
+  __syncthreads();
 
-    // S^T = K Q^T for 4 blocks of 32 keys
-    f32x16 s[4];
+  for (int it = 0; it < n_t; ++it) {
+    const int buf = it & 1;
+    const unsigned char *kd = lds + buf * C::BUF_BYTES;
+    const unsigned char *vd = kd + C::TILE_BYTES;
+    const int32_t vcj = a.valid_count[list[t_begin + it]];
+
+    // S^T = K Q^T over this wave's 64 keys (two 32-key blocks)
+    f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kh * 64 + kb * 32 + l32;
+        const int c = 2 * ks + g;
         const bf16x8 A = *reinterpret_cast<const bf16x8 *>(
-            k_lds + (kb * 32 + l32) * C::KPITCH + (ks * 16 + g * 8) * 2);
+            kd + row * C::ROW_BYTES + ((c ^ swz_k<D>(row)) << 4));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[ks], s[kb], 0, 0, 0);
       }
+
+    // stage tile it+1 into the free buffer (its last readers finished before
+    // the barrier that ended the previous iteration), then start tile it+2
+    if (it + 1 < n_t) {
+      store_tile(buf ^ 1);
+      if (it + 2 < n_t) issue_loads(rows_after);
+      rows_after = fetch_rows(it + 3);
     }
+
     if (vcj < VEDA_TILE) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+          const int key = kh * 64 + kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
           if (key >= vcj) s[kb][i] = -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float rs = 0.0f;
-    bf16x8 pb[4][2];
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+    // Lazy rescale: keep the running max unless this tile exceeds it by more
+    // than 2^8; probabilities then stay <= 256, exact in fp32 and bf16 range.
+    if (mx > m_run + 8.0f) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+      m_run = mx;
+      l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    // a key half that has seen only padding keeps m_run = -inf; its scores
+    // are all -inf then, and exp2(-inf - 0) = 0 avoids -inf + inf
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+    float rs = 0.0f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_new));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_use));
         rs += p;
         pb[kb][i / 8][i % 8] = static_cast<__bf16>(p);
       }
-    rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    l_run += rs + __shfl_xor(rs, 32, 64);
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T over the wave's 64 keys (4 k-steps of 16)
+    const int G = lane >> 4, s16 = lane & 15;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int kstep = 0; kstep < 4; ++kstep) {
+      const int kb = kstep >> 1, e = kstep & 1;
+      const int row0 = kh * 64 + kb * 32 + e * 16 + 4 * (G >> 1) + (s16 >> 2);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8 *>(
-              v_lds + (db * 32 + l32) * C::VPITCH + (kb * 32 + e * 16 + g * 8) * 2);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, pb[kb][e], o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < C::DB; ++db) {
+        const int d = db * 32 + 16 * (G & 1) + 4 * (s16 & 3);
+        const int c = d >> 3, h8 = (d >> 2) & 1;
+        const s16x4 lo = ds_read_tr(vd + row0 * C::ROW_BYTES + ((c ^ swz_v<D>(row0)) << 4) + h8 * 8);
+        const int row1 = row0 + 8;
+        const s16x4 hi4 = ds_read_tr(vd + row1 * C::ROW_BYTES + ((c ^ swz_v<D>(row1)) << 4) + h8 * 8);
+        const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
+                                                              hi4[0], hi4[1], hi4[2], hi4[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[kb][e],
+                                                       o[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();
   }
 
-  if (qrow < 0) return;
-  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  // Merge the two key halves: waves 4..7 hand (m, l, O^T) to waves 0..3.
+  float *xm = reinterpret_cast<float *>(lds);                    // [4][64] m, then [4][64] l
+  float *xo = xm + 2 * 4 * 64;                                   // [4][DB*16][64]
+  if (kh == 1) {
+    xm[qg * 64 + lane] = m_run;
+    xm[256 + qg * 64 + lane] = l_run;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xo[(qg * C::DB * 16 + db * 16 + i) * 64 + lane] = o[db][i];
+  }
+  __syncthreads();
+  if (kh == 1 || qrow < 0) return;
+  const float m1 = xm[qg * 64 + lane], l1 = xm[256 + qg * 64 + lane];
+  const float m = fmaxf(m_run, m1);
+  const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+  const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+  const float l = l_run * a0 + l1 * a1;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   uint16_t *ob = static_cast<uint16_t *>(a.out) + int64_t(qrow) * a.out_stride_s +
                  int64_t(heads.h[hi]) * a.out_stride_h;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int d = db * 32 + 8 * p + 4 * g;
       uint16_t h4[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        h4[r] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o[db][4 * p + r] * inv));
+      for (int r = 0; r < 4; ++r) {
+        const float o1 = xo[(qg * C::DB * 16 + db * 16 + 4 * p + r) * 64 + lane];
+        const float v = (o[db][4 * p + r] * a0 + o1 * a1) * inv;
+        h4[r] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+      }
       uint2 w;
       w.x = uint32_t(h4[0]) | (uint32_t(h4[1]) << 16);
       w.y = uint32_t(h4[2]) | (uint32_t(h4[3]) << 16);
@@ -268,10 +333,20 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
 hipError_t launch_attend_bf16(const AttendArgs &a, const HeadList &heads, int head_dim,
                               hipStream_t s) {
   const dim3 grid(grid_blocks(a));
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(256), 0, s, a, heads);
-  else
-    hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(256), 0, s, a, heads);
+  hipError_t e;
+  if (head_dim == 128) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(attend_bf16_kernel<128>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Bf16Cfg<128>::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(512), Bf16Cfg<128>::LDS_BYTES, s, a,
+                       heads);
+  } else {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(attend_bf16_kernel<64>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Bf16Cfg<64>::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(512), Bf16Cfg<64>::LDS_BYTES, s, a,
+                       heads);
+  }
   return hipGetLastError();
 }
 
