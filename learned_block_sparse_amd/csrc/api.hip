@@ -217,6 +217,15 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
   HeadList hl;
   st = fill_heads(heads, sel->n_heads, n_heads_total, &hl);
   if (st != VEDA_OK) return st;
+  // K/V rows are read with 32-bit offsets from each head's first element.
+  const int64_t elt = dtype == VEDA_BF16 ? 2 : 4;
+  const int64_t kv_extent = ((info->seq_len - 1) * stride_s + D) * elt;
+  if (dtype == VEDA_BF16 && kv_extent > int64_t(0xE0000000))
+    return fail(VEDA_ERR_UNSUPPORTED, "q/k/v rows of one head span more than 3.5 GiB");
+  // Padding rows are read at offset (2^32 - row pitch + chunk), which must fall
+  // past the range above: rows may not overlap and the pitch stays modest.
+  if (dtype == VEDA_BF16 && (stride_s < D || stride_s * 2 > (int64_t(1) << 29)))
+    return fail(VEDA_ERR_UNSUPPORTED, "bf16 attend needs D <= stride_s <= 2^28 elements");
   if (!(scale > 0.0f)) scale = float(1.0 / std::sqrt(double(D)));
   AttendArgs a;
   a.q = q;
@@ -235,6 +244,7 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
   a.n_heads = sel->n_heads;
   a.n_tiles = info->n_tiles;
   a.n_video = info->n_video;
+  a.kv_bytes = uint32_t(kv_extent);
   a.scale = scale;
   a.scale_log2 = float(double(scale) * 1.4426950408889634);
   hipError_t e = dtype == VEDA_BF16 ? launch_attend_bf16(a, hl, D, stream)

@@ -62,35 +62,35 @@ __host__ inline uint32_t grid_blocks(const AttendArgs &a) {
 // --------------------------------------------------------------- bf16 MFMA --
 // 8 wavefronts (2 per SIMD): wave w takes query rows 32*(w%4) .. +31 and key
 // half w/4 (keys 64*(w/4) .. +63) of every kept tile, with its own online
-// softmax state; the two halves are merged through LDS at the end. Two
-// waves per SIMD let one wave's softmax (VALU) run while the other's MFMAs
-// execute.
+// softmax state; the two halves are merged through LDS at the end.
 //
-// K and V tiles are double-buffered in LDS, row-major, each 16-byte chunk c of
-// row r stored at chunk position c ^ swz(r) so that both access patterns are
-// free of bank conflicts:
+// K and V tiles arrive in LDS by direct buffer-to-LDS loads (no register
+// staging) into four separate arrays K0, K1, V0, V1 (double buffers). Such a
+// load writes 64 lanes x 16 bytes contiguously, so rows are stored unpadded
+// and each 16-byte chunk c of row r sits at chunk position c ^ swz(r), which
+// keeps both read patterns free of bank conflicts (64 banks):
 //   K: the A operand of S^T = K Q^T, one 16-byte read of 8 d-values per lane
-//      for 32 consecutive rows;
+//      across 32 consecutive rows (swz spreads 16 consecutive rows over all
+//      16 positions);
 //   V: the A operand of O^T += V^T P^T, built by ds_read_b64_tr_b16. Within a
 //      16-lane group that instruction hands lane i, element j, the (i%4)-th
 //      16-bit value of the 8 bytes addressed by lane i/4 + 4j; with source
 //      lane s pointing at row (key) k0 + s/4, columns d0 + 4*(s%4), lane i
-//      receives V[k0 + j][d0 + i] for j = 0..3: four keys of one column.
-// Tiles are staged through registers: the loads of tile t+2's rows are
-// issued while tile t is computed and written to the free buffer one
-// iteration later, so no wave waits on a global load it just issued. The
-// row ids (perm) are fetched one tile further ahead, one per lane, and
-// broadcast within the wave by shuffles.
+//      receives V[k0 + j][d0 + i] for j = 0..3: four keys of one column (swz
+//      gives the four rows of a read disjoint chunk positions).
+// Rows are fetched with 32-bit offsets from a per-head buffer descriptor; a
+// padding slot gets an offset past the descriptor's range, which the
+// hardware returns as zeros (the page's tile-ordered copies hold zeros in
+// padding slots).
 template <int D>
 struct Bf16Cfg {
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int CHUNKS = D / 8;                        // 16-byte chunks per row
-  static constexpr int TILE_BYTES = VEDA_TILE * ROW_BYTES;
-  static constexpr int BUF_BYTES = 2 * TILE_BYTES;            // K then V
-  static constexpr int LDS_BYTES = 2 * BUF_BYTES;             // double-buffered
-  static constexpr int ROWS_PER_LOAD = 64 / CHUNKS;           // rows one 64-lane load covers
-  static constexpr int LOADS = 16 / ROWS_PER_LOAD;            // loads per wave per tensor
-  static constexpr int DB = D / 32;                           // 32-wide d blocks of O^T
+  static constexpr int ROW = D * 2;                          // bytes per row
+  static constexpr int TILE_BYTES = VEDA_TILE * ROW;
+  static constexpr int ROWS_PER_LOAD = 1024 / ROW;           // rows one 64-lane load covers
+  static constexpr int LOADS = 16 / ROWS_PER_LOAD;           // loads per wave per tensor
+  static constexpr int CHUNKS = D / 8;                       // 16-byte chunks per row
+  static constexpr int DB = D / 32;                          // 32-wide d blocks of O^T
+  static constexpr int KS = D / 16;                          // 16-wide k steps of S^T
 };
 
 template <int D>
@@ -104,12 +104,24 @@ __device__ inline int swz_v(int row) {
 
 __device__ inline uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
-// Rows of padding slots read zeros from here, as the page's tile-ordered
-// copies hold zeros in padding slots.
-__device__ __attribute__((aligned(16))) uint16_t g_zero_row[128] = {};
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Exchange with the lane 32 apart through v_permlane32_swap (VALU; no LDS
+// round trip): with both operands x, the two results hold x from each half,
+// so their max / sum is the same in lanes l and l + 32.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline s16x4 ds_read_tr(const unsigned char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
@@ -118,18 +130,25 @@ __device__ inline s16x4 ds_read_tr(const unsigned char *p) {
 template <int D>
 __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadList heads) {
   using C = Bf16Cfg<D>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  __shared__ __attribute__((aligned(1024))) unsigned char K0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char K1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char V0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char V1[C::TILE_BYTES];
 
   const BlockMap bm = map_block(a, blockIdx.x);
   if (!bm.live) return;
   const int hi = bm.hi, tile = bm.tile;
   const int64_t hoff = int64_t(heads.h[hi]) * a.stride_h;
   const uint16_t *qb = static_cast<const uint16_t *>(a.q) + hoff;
-  const uint16_t *kb_ = static_cast<const uint16_t *>(a.k) + hoff;
-  const uint16_t *vb = static_cast<const uint16_t *>(a.v) + hoff;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(static_cast<const uint16_t *>(a.k) + hoff), 0, int(a.kv_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(static_cast<const uint16_t *>(a.v) + hoff), 0, int(a.kv_bytes), 0x00020000);
+  const uint32_t row_bytes = uint32_t(a.stride_s) * 2u;
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // scalar: LDS bases stay in SGPRs
+  const int lane = tid % 64;
   const int g = lane / 32, l32 = lane % 32;
   const int qg = wave & 3, kh = wave >> 2;
 
@@ -137,9 +156,9 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
   const int32_t vc_q = a.valid_count[tile];
   const int qi = qg * 32 + l32;
   const int32_t qrow = qi < vc_q ? a.perm[int64_t(tile) * VEDA_TILE + qi] : -1;
-  bf16x8 qf[D / 16];
+  bf16x8 qf[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
+  for (int ks = 0; ks < C::KS; ++ks) {
     uint4 u = make_uint4(0, 0, 0, 0);
     if (qrow >= 0) u = ld16(qb + int64_t(qrow) * a.stride_s + ks * 16 + g * 8);
     qf[ks] = __builtin_bit_cast(bf16x8, u);
@@ -156,92 +175,136 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
   const int32_t *list = a.cols + int64_t(hi) * a.entries_per_head;
   const int n_t = t_end - t_begin;
 
-  // Row ids: lane holds perm[j*128 + 16*wave + lane%16] of a tile j.
-  auto fetch_rows = [&](int idx) -> int32_t {
-    if (idx >= n_t) return -1;
-    const int32_t j = list[t_begin + idx];
-    return a.perm[int64_t(j) * VEDA_TILE + 16 * wave + (lane & 15)];
+  // Load mapping: wave w fills rows 16w .. 16w+15 of a tile with LOADS
+  // direct loads per tensor; load i lands at bytes (16w + R*i)*ROW + 16*lane
+  // (R = rows per load), i.e. row 16w + R*i + lane/CHUNKS, chunk position
+  // lane%CHUNKS, which holds global chunk position ^ swz(row).
+  const int ld_row = lane / C::CHUNKS, ld_pos = lane % C::CHUNKS;
+  uint32_t k_chunk[C::LOADS], v_chunk[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int row = 16 * wave + C::ROWS_PER_LOAD * i + ld_row;
+    k_chunk[i] = 16u * uint32_t(ld_pos ^ swz_k<D>(row));
+    v_chunk[i] = 16u * uint32_t(ld_pos ^ swz_v<D>(row));
+  }
+  // Row ids of the LOADS rows this lane fetches in a tile (-1 on padding).
+  struct Rows {
+    int32_t r[C::LOADS];
   };
-  uint4 kreg[C::LOADS], vreg[C::LOADS];
-  auto issue_loads = [&](int32_t rows) {
+  auto rows_of = [&](int32_t j) {
+    Rows out;
+    const int32_t *pj = a.perm + int64_t(j) * VEDA_TILE + 16 * wave + ld_row;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) out.r[i] = pj[C::ROWS_PER_LOAD * i];
+    return out;
+  };
+  // Byte offsets are formed only when the loads are issued, an iteration
+  // after the row ids were fetched, so fetching row ids never stalls a wave.
+  // A padding row (id -1) gives 2^32 - row_bytes + chunk, past the
+  // descriptor's range (the host keeps row_bytes <= 2^29, every chunk below
+  // row_bytes and the range below 0xE0000000), so it reads as zeros.
+  auto dma = [&](const __amdgpu_buffer_rsrc_t &rsrc, unsigned char *dst, const Rows &rows,
+                 const uint32_t (&chunk)[C::LOADS]) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int r = C::ROWS_PER_LOAD * i + lane / C::CHUNKS;   // row within the wave's 16
-      const int c = lane % C::CHUNKS;
-      const int32_t rid = __shfl(rows, r, 64);
-      const uint16_t *ks = rid >= 0 ? kb_ + int64_t(rid) * a.stride_s + c * 8 : g_zero_row + c * 8;
-      const uint16_t *vs = rid >= 0 ? vb + int64_t(rid) * a.stride_s + c * 8 : g_zero_row + c * 8;
-      kreg[i] = ld16(ks);
-      vreg[i] = ld16(vs);
+      const uint32_t off = uint32_t(rows.r[i]) * row_bytes + chunk[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_void *)(dst + (16 * wave + C::ROWS_PER_LOAD * i) * C::ROW), 16, off, 0, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-    unsigned char *kd = lds + buf * C::BUF_BYTES;
-    unsigned char *vd = kd + C::TILE_BYTES;
+
+  // Compute-side read offsets (per lane; swizzled positions).
+  // K: row kh*64 + kb*32 + l32, chunk 2ks + g -> position (2ks + g) ^ swz(row);
+  // swz(row) depends only on l32, so the offset is base ^ (32 ks) per k step.
+  const int krow = kh * 64 + l32;
+  const uint32_t k_base = uint32_t(krow * C::ROW);
+  const uint32_t k_sw = uint32_t(swz_k<D>(krow));
+  uint32_t k_off[C::KS];
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int row = 16 * wave + C::ROWS_PER_LOAD * i + lane / C::CHUNKS;
-      const int c = lane % C::CHUNKS;
-      *reinterpret_cast<uint4 *>(kd + row * C::ROW_BYTES + ((c ^ swz_k<D>(row)) << 4)) = kreg[i];
-      *reinterpret_cast<uint4 *>(vd + row * C::ROW_BYTES + ((c ^ swz_v<D>(row)) << 4)) = vreg[i];
-    }
-  };
+  for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = k_base + 16u * ((uint32_t(2 * ks + g)) ^ k_sw);
+  // V: rows kh*64 + kb*32 + e*16 + 4*(G/2) + s16/4 (+8 for the upper four
+  // keys), columns db*32 + 16*(G%2) + 4*(s16%4).
+  const int G = lane >> 4, s16 = lane & 15;
+  const int vrow = kh * 64 + 4 * (G >> 1) + (s16 >> 2);
+  const int vcol = 16 * (G & 1) + 4 * (s16 & 3);
+  uint32_t v_off[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    const int d = db * 32 + vcol;
+    v_off[db] = uint32_t(vrow * C::ROW) + 16u * uint32_t((d >> 3) ^ swz_v<D>(vrow)) + 8u * ((d >> 2) & 1);
+  }
 
-  // prologue: tile 0 staged into buffer 0, tile 1's loads in flight
-  int32_t rows_next = fetch_rows(0);
-  issue_loads(rows_next);
-  rows_next = fetch_rows(1);
-  store_tile(0);
-  int32_t rows_after = fetch_rows(2);
-  if (n_t > 1) issue_loads(rows_next);
-  __syncthreads();
+  // List positions past the end read the last entry again: the extra tiles
+  // are loaded and discarded, which keeps the pipeline free of branches.
+  auto list_at = [&](int idx) -> int32_t { return list[t_begin + min(idx, n_t - 1)]; };
 
-  for (int it = 0; it < n_t; ++it) {
-    const int buf = it & 1;
-    const unsigned char *kd = lds + buf * C::BUF_BYTES;
-    const unsigned char *vd = kd + C::TILE_BYTES;
-    const int32_t vcj = a.valid_count[list[t_begin + it]];
-
-    // S^T = K Q^T over this wave's 64 keys (two 32-key blocks)
-    f32x16 s[2];
+  // S^T = K Q^T over this wave's 64 keys of the tile in `kbuf`
+  auto scores = [&](const unsigned char *kbuf, f32x16 (&sn)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) sn[kb][i] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int row = kh * 64 + kb * 32 + l32;
-        const int c = 2 * ks + g;
-        const bf16x8 A = *reinterpret_cast<const bf16x8 *>(
-            kd + row * C::ROW_BYTES + ((c ^ swz_k<D>(row)) << 4));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[ks], s[kb], 0, 0, 0);
+        const bf16x8 A = *reinterpret_cast<const bf16x8 *>(kbuf + k_off[ks] + kb * 32 * C::ROW);
+        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[ks], sn[kb], 0, 0, 0);
       }
+  };
 
-    // stage tile it+1 into the free buffer (its last readers finished before
-    // the barrier that ended the previous iteration), then start tile it+2
-    if (it + 1 < n_t) {
-      store_tile(buf ^ 1);
-      if (it + 2 < n_t) issue_loads(rows_after);
-      rows_after = fetch_rows(it + 3);
-    }
+  // Pipeline. At the top of iteration t (after a barrier): S(t) is in
+  // registers, K(t+1) and V(t) are in LDS (K buffer (t+1)%2, V buffer t%2),
+  // and the row ids of tiles t+1 and t+2 are known. Iteration t starts the
+  // loads of K(t+2) into K buffer t%2 (last read by S(t), an iteration ago)
+  // and V(t+1) into V buffer (t+1)%2 (last read by P(t-1)V(t-1)), forms S(t+1)
+  // interleaved with the softmax of tile t, then P(t)V(t), and fetches the
+  // row ids of tile t+3. The barrier closing the iteration waits for its own
+  // loads, so they have the whole iteration to land.
+  f32x16 sA[2], sB[2];
+  Rows rows1 = rows_of(list_at(1)), rows2 = rows_of(list_at(2));
+  {
+    const Rows rows0 = rows_of(list_at(0));
+    dma(rk, K0, rows0, k_chunk);
+    dma(rv, V0, rows0, v_chunk);
+    dma(rk, K1, rows1, k_chunk);
+    __syncthreads();
+    scores(K0, sA);
+  }
+  int32_t j3 = list_at(3);
+  int32_t vc0 = a.valid_count[list_at(0)], vc1 = a.valid_count[list_at(1)],
+          vc2 = a.valid_count[list_at(2)];
+  __syncthreads();
 
-    if (vcj < VEDA_TILE) {
+  auto iteration = [&](const int t, unsigned char *kn, unsigned char *kfree,
+                       const unsigned char *vcur, unsigned char *vfree, f32x16 (&sc)[2],
+                       f32x16 (&sn)[2]) {
+    dma(rk, kfree, rows2, k_chunk);
+    dma(rv, vfree, rows1, v_chunk);
+    rows1 = rows2;
+    rows2 = rows_of(j3);
+    const int32_t vc_new = a.valid_count[j3];
+    j3 = list_at(t + 4);
+
+    // mask padding keys of tile t (only partial tiles; the empty asm keeps
+    // the branch from being flattened into selects on every tile)
+    if (vc0 < VEDA_TILE) {
+      asm volatile("" ::: "memory");
+      // key kh*64 + 4g + (kb*32 + 8(i/4) + i%4) is padding when the constant
+      // part reaches vc0 - (kh*64 + 4g)
+      const int thr = vc0 - (kh * 64 + 4 * g);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kh * 64 + kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
-          if (key >= vcj) s[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 8 * (i / 4) + (i % 4) >= thr) sc[kb][i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+    mx = pair_max(mx) * a.scale_log2;
     // Lazy rescale: keep the running max unless this tile exceeds it by more
     // than 2^8; probabilities then stay <= 256, exact in fp32 and bf16 range.
     if (mx > m_run + 8.0f) {
@@ -256,54 +319,91 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
     // a key half that has seen only padding keeps m_run = -inf; its scores
     // are all -inf then, and exp2(-inf - 0) = 0 avoids -inf + inf
     const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-    float rs = 0.0f;
+
+    // S(t+1): independent of the softmax below, so its MFMAs overlap it
+    scores(kn, sn);
+
     bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_use));
-        rs += p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], a.scale_log2, -m_use));
         pb[kb][i / 8][i % 8] = static_cast<__bf16>(p);
       }
-    l_run += rs + __shfl_xor(rs, 32, 64);
+    // row sum of the bf16 probabilities that enter P V
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const bf16x2 pr = {pb[kb][e][2 * q2], pb[kb][e][2 * q2 + 1]};
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+        }
+    l_run += pair_sum(rs);
 
-    // O^T += V^T P^T over the wave's 64 keys (4 k-steps of 16)
-    const int G = lane >> 4, s16 = lane & 15;
+    // O^T += V^T P^T over the wave's 64 keys of tile t (4 k-steps of 16)
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
       const int kb = kstep >> 1, e = kstep & 1;
-      const int row0 = kh * 64 + kb * 32 + e * 16 + 4 * (G >> 1) + (s16 >> 2);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const int d = db * 32 + 16 * (G & 1) + 4 * (s16 & 3);
-        const int c = d >> 3, h8 = (d >> 2) & 1;
-        const s16x4 lo = ds_read_tr(vd + row0 * C::ROW_BYTES + ((c ^ swz_v<D>(row0)) << 4) + h8 * 8);
-        const int row1 = row0 + 8;
-        const s16x4 hi4 = ds_read_tr(vd + row1 * C::ROW_BYTES + ((c ^ swz_v<D>(row1)) << 4) + h8 * 8);
+        const unsigned char *p0 = vcur + v_off[db] + (kb * 32 + e * 16) * C::ROW;
+        const s16x4 lo = ds_read_tr(p0);
+        const s16x4 hi4 = ds_read_tr(p0 + 8 * C::ROW);
         const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
                                                               hi4[0], hi4[1], hi4[2], hi4[3]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[kb][e],
                                                        o[db], 0, 0, 0);
       }
     }
+    vc0 = vc1;
+    vc1 = vc2;
+    vc2 = vc_new;
+    // Instruction order for the block above: each S(t+1) MFMA with the read
+    // of a K fragment and a few softmax VALU ops, then each P V MFMA with its
+    // two transposed reads. Groups: 0x100 LDS read, 0x008 MFMA, 0x002 VALU.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * C::DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    }
     __syncthreads();
-  }
+  };
 
-  // Merge the two key halves: waves 4..7 hand (m, l, O^T) to waves 0..3.
-  float *xm = reinterpret_cast<float *>(lds);                    // [4][64] m, then [4][64] l
-  float *xo = xm + 2 * 4 * 64;                                   // [4][DB*16][64]
+  int t = 0;
+  for (; t + 1 < n_t; t += 2) {
+    iteration(t, K1, K0, V0, V1, sA, sB);
+    iteration(t + 1, K0, K1, V1, V0, sB, sA);
+  }
+  if (t < n_t) iteration(t, K1, K0, V0, V1, sA, sB);
+
+  // Merge the two key halves: waves 4..7 hand (m, l, O^T) to waves 0..3,
+  // through K0/K1 (O^T, 16 KB per wave) and V0 (m, l).
+  float *xm = reinterpret_cast<float *>(V0) + qg * 128;
+  float *xo = reinterpret_cast<float *>((qg < 2 ? K0 : K1) + (qg & 1) * (C::DB * 16 * 64 * 4));
   if (kh == 1) {
-    xm[qg * 64 + lane] = m_run;
-    xm[256 + qg * 64 + lane] = l_run;
+    xm[lane] = m_run;
+    xm[64 + lane] = l_run;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xo[(qg * C::DB * 16 + db * 16 + i) * 64 + lane] = o[db][i];
+      for (int i = 0; i < 16; ++i) xo[(db * 16 + i) * 64 + lane] = o[db][i];
   }
   __syncthreads();
   if (kh == 1 || qrow < 0) return;
-  const float m1 = xm[qg * 64 + lane], l1 = xm[256 + qg * 64 + lane];
+  const float m1 = xm[lane], l1 = xm[64 + lane];
   const float m = fmaxf(m_run, m1);
   const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
   const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
@@ -319,7 +419,7 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
       uint16_t h4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float o1 = xo[(qg * C::DB * 16 + db * 16 + 4 * p + r) * 64 + lane];
+        const float o1 = xo[(db * 16 + 4 * p + r) * 64 + lane];
         const float v = (o[db][4 * p + r] * a0 + o1 * a1) * inv;
         h4[r] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
       }
@@ -333,20 +433,10 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
 hipError_t launch_attend_bf16(const AttendArgs &a, const HeadList &heads, int head_dim,
                               hipStream_t s) {
   const dim3 grid(grid_blocks(a));
-  hipError_t e;
-  if (head_dim == 128) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(attend_bf16_kernel<128>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, Bf16Cfg<128>::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(512), Bf16Cfg<128>::LDS_BYTES, s, a,
-                       heads);
-  } else {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(attend_bf16_kernel<64>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, Bf16Cfg<64>::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(512), Bf16Cfg<64>::LDS_BYTES, s, a,
-                       heads);
-  }
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(512), 0, s, a, heads);
+  else
+    hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(512), 0, s, a, heads);
   return hipGetLastError();
 }
 

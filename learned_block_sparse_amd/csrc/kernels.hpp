@@ -79,6 +79,7 @@ struct AttendArgs {
   const int32_t *perm, *valid_count, *row_offsets, *cols;
   int64_t entries_per_head;
   int32_t n_heads, n_tiles, n_video;
+  uint32_t kv_bytes;         // bytes from a head's first K/V element to the end of its last row
   float scale_log2;          // softmax scale * log2(e)
   float scale;               // softmax scale
 };
