@@ -366,17 +366,20 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
     // Instruction order for the block above: each S(t+1) MFMA with the read
     // of a K fragment and a few softmax VALU ops, then each P V MFMA with its
     // two transposed reads. Groups: 0x100 LDS read, 0x008 MFMA, 0x002 VALU.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    // LDS reads run ahead of the MFMAs that consume them (four K fragments
+    // first; the spare read slots of the S phase start on V fragments).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 2 * C::KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < 4 * C::DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
     __syncthreads();
