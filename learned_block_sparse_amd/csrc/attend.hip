@@ -60,15 +60,17 @@ __host__ inline uint32_t grid_blocks(const AttendArgs &a) {
 }
 
 // --------------------------------------------------------------- bf16 MFMA --
-// 8 wavefronts (2 per SIMD): wave w takes query rows 32*(w%4) .. +31 and key
-// half w/4 (keys 64*(w/4) .. +63) of every kept tile, with its own online
-// softmax state; the two halves are merged through LDS at the end.
+// 4 wavefronts per workgroup, two workgroups per CU (one wave of each on
+// every SIMD): wave w takes query rows 32w .. 32w+31 and all 128 keys of
+// every kept tile, so each wave owns its rows' softmax state outright and no
+// merge is needed. The two workgroups keep their own barriers; their phases
+// drift apart, so one group's MFMAs overlap the other's softmax.
 //
 // K and V tiles arrive in LDS by direct buffer-to-LDS loads (no register
-// staging) into four separate arrays K0, K1, V0, V1 (double buffers). Such a
-// load writes 64 lanes x 16 bytes contiguously, so rows are stored unpadded
-// and each 16-byte chunk c of row r sits at chunk position c ^ swz(r), which
-// keeps both read patterns free of bank conflicts (64 banks):
+// staging) into one K and one V array per workgroup. Such a load writes 64
+// lanes x 16 bytes contiguously, so rows are stored unpadded and each
+// 16-byte chunk c of row r sits at chunk position c ^ swz(r), which keeps
+// both read patterns free of bank conflicts (64 banks):
 //   K: the A operand of S^T = K Q^T, one 16-byte read of 8 d-values per lane
 //      across 32 consecutive rows (swz spreads 16 consecutive rows over all
 //      16 positions);
@@ -128,12 +130,10 @@ __device__ inline s16x4 ds_read_tr(const unsigned char *p) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadList heads) {
+__global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadList heads) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char K0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char K1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char V0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char V1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char Kb[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vb[C::TILE_BYTES];
 
   const BlockMap bm = map_block(a, blockIdx.x);
   if (!bm.live) return;
@@ -150,11 +150,10 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // scalar: LDS bases stay in SGPRs
   const int lane = tid % 64;
   const int g = lane / 32, l32 = lane % 32;
-  const int qg = wave & 3, kh = wave >> 2;
 
   // Q fragment (B operand of S^T = K Q^T): q[row][16*ks + 8*g .. +8]
   const int32_t vc_q = a.valid_count[tile];
-  const int qi = qg * 32 + l32;
+  const int qi = wave * 32 + l32;
   const int32_t qrow = qi < vc_q ? a.perm[int64_t(tile) * VEDA_TILE + qi] : -1;
   bf16x8 qf[C::KS];
 #pragma unroll
@@ -175,57 +174,49 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
   const int32_t *list = a.cols + int64_t(hi) * a.entries_per_head;
   const int n_t = t_end - t_begin;
 
-  // Load mapping: wave w fills rows 16w .. 16w+15 of a tile with LOADS
-  // direct loads per tensor; load i lands at bytes (16w + R*i)*ROW + 16*lane
-  // (R = rows per load), i.e. row 16w + R*i + lane/CHUNKS, chunk position
+  // Load mapping: wave w fills rows 32w .. 32w+31 of a tile with 2*LOADS
+  // direct loads per tensor; load i lands at bytes (32w + R*i)*ROW + 16*lane
+  // (R = rows per load), i.e. row 32w + R*i + lane/CHUNKS, chunk position
   // lane%CHUNKS, which holds global chunk position ^ swz(row).
+  constexpr int NL = 2 * C::LOADS;
   const int ld_row = lane / C::CHUNKS, ld_pos = lane % C::CHUNKS;
-  uint32_t k_chunk[C::LOADS], v_chunk[C::LOADS];
+  uint32_t k_chunk[NL], v_chunk[NL];
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int row = 16 * wave + C::ROWS_PER_LOAD * i + ld_row;
+  for (int i = 0; i < NL; ++i) {
+    const int row = 32 * wave + C::ROWS_PER_LOAD * i + ld_row;
     k_chunk[i] = 16u * uint32_t(ld_pos ^ swz_k<D>(row));
     v_chunk[i] = 16u * uint32_t(ld_pos ^ swz_v<D>(row));
   }
-  // Row ids of the LOADS rows this lane fetches in a tile (-1 on padding).
   struct Rows {
-    int32_t r[C::LOADS];
+    int32_t r[NL];
   };
   auto rows_of = [&](int32_t j) {
     Rows out;
-    const int32_t *pj = a.perm + int64_t(j) * VEDA_TILE + 16 * wave + ld_row;
+    const int32_t *pj = a.perm + int64_t(j) * VEDA_TILE + 32 * wave + ld_row;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) out.r[i] = pj[C::ROWS_PER_LOAD * i];
+    for (int i = 0; i < NL; ++i) out.r[i] = pj[C::ROWS_PER_LOAD * i];
     return out;
   };
-  // Byte offsets are formed only when the loads are issued, an iteration
-  // after the row ids were fetched, so fetching row ids never stalls a wave.
   // A padding row (id -1) gives 2^32 - row_bytes + chunk, past the
   // descriptor's range (the host keeps row_bytes <= 2^29, every chunk below
   // row_bytes and the range below 0xE0000000), so it reads as zeros.
   auto dma = [&](const __amdgpu_buffer_rsrc_t &rsrc, unsigned char *dst, const Rows &rows,
-                 const uint32_t (&chunk)[C::LOADS]) {
+                 const uint32_t (&chunk)[NL]) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
+    for (int i = 0; i < NL; ++i) {
       const uint32_t off = uint32_t(rows.r[i]) * row_bytes + chunk[i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (lds_void *)(dst + (16 * wave + C::ROWS_PER_LOAD * i) * C::ROW), 16, off, 0, 0, 0);
+          rsrc, (lds_void *)(dst + (32 * wave + C::ROWS_PER_LOAD * i) * C::ROW), 16, off, 0, 0, 0);
     }
   };
 
   // Compute-side read offsets (per lane; swizzled positions).
-  // K: row kh*64 + kb*32 + l32, chunk 2ks + g -> position (2ks + g) ^ swz(row);
-  // swz(row) depends only on l32, so the offset is base ^ (32 ks) per k step.
-  const int krow = kh * 64 + l32;
-  const uint32_t k_base = uint32_t(krow * C::ROW);
-  const uint32_t k_sw = uint32_t(swz_k<D>(krow));
+  const uint32_t k_sw = uint32_t(swz_k<D>(l32));
   uint32_t k_off[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = k_base + 16u * ((uint32_t(2 * ks + g)) ^ k_sw);
-  // V: rows kh*64 + kb*32 + e*16 + 4*(G/2) + s16/4 (+8 for the upper four
-  // keys), columns db*32 + 16*(G%2) + 4*(s16%4).
+  for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = uint32_t(l32 * C::ROW) + 16u * ((uint32_t(2 * ks + g)) ^ k_sw);
   const int G = lane >> 4, s16 = lane & 15;
-  const int vrow = kh * 64 + 4 * (G >> 1) + (s16 >> 2);
+  const int vrow = 4 * (G >> 1) + (s16 >> 2);
   const int vcol = 16 * (G & 1) + 4 * (s16 & 3);
   uint32_t v_off[C::DB];
 #pragma unroll
@@ -234,76 +225,61 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
     v_off[db] = uint32_t(vrow * C::ROW) + 16u * uint32_t((d >> 3) ^ swz_v<D>(vrow)) + 8u * ((d >> 2) & 1);
   }
 
-  // List positions past the end read the last entry again: the extra tiles
-  // are loaded and discarded, which keeps the pipeline free of branches.
   auto list_at = [&](int idx) -> int32_t { return list[t_begin + min(idx, n_t - 1)]; };
 
-  // S^T = K Q^T over this wave's 64 keys of the tile in `kbuf`
-  auto scores = [&](const unsigned char *kbuf, f32x16 (&sn)[2]) {
+  // Per tile: S(t) from K -> barrier, start K(t+1) -> softmax(t) -> P(t)V(t)
+  // from V -> barrier, start V(t+1). Each barrier also waits for the loads
+  // started at the previous one, so K(t+1) has the softmax and P V phases to
+  // land and V(t+1) the next S and softmax phases. Two workgroups share a CU
+  // and keep their own barriers, so their phases drift apart and one group's
+  // MFMAs overlap the other's vector work.
+  Rows rows_next = rows_of(list_at(1));
+  {
+    const Rows rows0 = rows_of(list_at(0));
+    dma(rk, Kb, rows0, k_chunk);
+    dma(rv, Vb, rows0, v_chunk);
+  }
+  int32_t j2 = list_at(2);
+  int32_t vc_cur = a.valid_count[list_at(0)], vc_next = a.valid_count[list_at(1)];
+  __syncthreads();
+
+  for (int t = 0; t < n_t; ++t) {
+    f32x16 s[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sn[kb][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8 *>(kbuf + k_off[ks] + kb * 32 * C::ROW);
-        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[ks], sn[kb], 0, 0, 0);
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8 *>(Kb + k_off[ks] + kb * 32 * C::ROW);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[ks], s[kb], 0, 0, 0);
       }
-  };
+    __syncthreads();   // every wave is done with K(t); V(t) has landed
+    // no load may still be writing LDS when the workgroup ends: the last
+    // tile starts none
+    const bool more = t + 1 < n_t;
+    if (more) dma(rk, Kb, rows_next, k_chunk);
+    const Rows rows_v = rows_next;
+    rows_next = rows_of(j2);
+    const int32_t vc_new = a.valid_count[j2];
+    j2 = list_at(t + 3);
 
-  // Pipeline. At the top of iteration t (after a barrier): S(t) is in
-  // registers, K(t+1) and V(t) are in LDS (K buffer (t+1)%2, V buffer t%2),
-  // and the row ids of tiles t+1 and t+2 are known. Iteration t starts the
-  // loads of K(t+2) into K buffer t%2 (last read by S(t), an iteration ago)
-  // and V(t+1) into V buffer (t+1)%2 (last read by P(t-1)V(t-1)), forms S(t+1)
-  // interleaved with the softmax of tile t, then P(t)V(t), and fetches the
-  // row ids of tile t+3. The barrier closing the iteration waits for its own
-  // loads, so they have the whole iteration to land.
-  f32x16 sA[2], sB[2];
-  Rows rows1 = rows_of(list_at(1)), rows2 = rows_of(list_at(2));
-  {
-    const Rows rows0 = rows_of(list_at(0));
-    dma(rk, K0, rows0, k_chunk);
-    dma(rv, V0, rows0, v_chunk);
-    dma(rk, K1, rows1, k_chunk);
-    __syncthreads();
-    scores(K0, sA);
-  }
-  int32_t j3 = list_at(3);
-  int32_t vc0 = a.valid_count[list_at(0)], vc1 = a.valid_count[list_at(1)],
-          vc2 = a.valid_count[list_at(2)];
-  __syncthreads();
-
-  auto iteration = [&](const int t, unsigned char *kn, unsigned char *kfree,
-                       const unsigned char *vcur, unsigned char *vfree, f32x16 (&sc)[2],
-                       f32x16 (&sn)[2]) {
-    dma(rk, kfree, rows2, k_chunk);
-    dma(rv, vfree, rows1, v_chunk);
-    rows1 = rows2;
-    rows2 = rows_of(j3);
-    const int32_t vc_new = a.valid_count[j3];
-    j3 = list_at(t + 4);
-
-    // mask padding keys of tile t (only partial tiles; the empty asm keeps
-    // the branch from being flattened into selects on every tile)
-    if (vc0 < VEDA_TILE) {
+    if (vc_cur < VEDA_TILE) {
       asm volatile("" ::: "memory");
-      // key kh*64 + 4g + (kb*32 + 8(i/4) + i%4) is padding when the constant
-      // part reaches vc0 - (kh*64 + 4g)
-      const int thr = vc0 - (kh * 64 + 4 * g);
+      const int thr = vc_cur - 4 * g;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (kb * 32 + 8 * (i / 4) + (i % 4) >= thr) sc[kb][i] = -INFINITY;
+          if (kb * 32 + 8 * (i / 4) + (i % 4) >= thr) s[kb][i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = pair_max(mx) * a.scale_log2;
     // Lazy rescale: keep the running max unless this tile exceeds it by more
     // than 2^8; probabilities then stay <= 256, exact in fp32 and bf16 range.
@@ -316,26 +292,18 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
-    // a key half that has seen only padding keeps m_run = -inf; its scores
-    // are all -inf then, and exp2(-inf - 0) = 0 avoids -inf + inf
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-
-    // S(t+1): independent of the softmax below, so its MFMAs overlap it
-    scores(kn, sn);
-
-    bf16x8 pb[2][2];
+    bf16x8 pb[4][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], a.scale_log2, -m_use));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_run));
         pb[kb][i / 8][i % 8] = static_cast<__bf16>(p);
       }
-    // row sum of the bf16 probabilities that enter P V
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     float rs = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int e = 0; e < 2; ++e)
 #pragma unroll
@@ -345,13 +313,12 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
         }
     l_run += pair_sum(rs);
 
-    // O^T += V^T P^T over the wave's 64 keys of tile t (4 k-steps of 16)
 #pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
+    for (int kstep = 0; kstep < 8; ++kstep) {
       const int kb = kstep >> 1, e = kstep & 1;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const unsigned char *p0 = vcur + v_off[db] + (kb * 32 + e * 16) * C::ROW;
+        const unsigned char *p0 = Vb + v_off[db] + (kb * 32 + e * 16) * C::ROW;
         const s16x4 lo = ds_read_tr(p0);
         const s16x4 hi4 = ds_read_tr(p0 + 8 * C::ROW);
         const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
@@ -360,58 +327,14 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
                                                        o[db], 0, 0, 0);
       }
     }
-    vc0 = vc1;
-    vc1 = vc2;
-    vc2 = vc_new;
-    // Instruction order for the block above: each S(t+1) MFMA with the read
-    // of a K fragment and a few softmax VALU ops, then each P V MFMA with its
-    // two transposed reads. Groups: 0x100 LDS read, 0x008 MFMA, 0x002 VALU.
-    // LDS reads run ahead of the MFMAs that consume them (four K fragments
-    // first; the spare read slots of the S phase start on V fragments).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * C::KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * C::DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-    }
-    __syncthreads();
-  };
-
-  int t = 0;
-  for (; t + 1 < n_t; t += 2) {
-    iteration(t, K1, K0, V0, V1, sA, sB);
-    iteration(t + 1, K0, K1, V1, V0, sB, sA);
+    __syncthreads();   // every wave is done with V(t); K(t+1) has landed
+    if (more) dma(rv, Vb, rows_v, v_chunk);
+    vc_cur = vc_next;
+    vc_next = vc_new;
   }
-  if (t < n_t) iteration(t, K1, K0, V0, V1, sA, sB);
 
-  // Merge the two key halves: waves 4..7 hand (m, l, O^T) to waves 0..3,
-  // through K0/K1 (O^T, 16 KB per wave) and V0 (m, l).
-  float *xm = reinterpret_cast<float *>(V0) + qg * 128;
-  float *xo = reinterpret_cast<float *>((qg < 2 ? K0 : K1) + (qg & 1) * (C::DB * 16 * 64 * 4));
-  if (kh == 1) {
-    xm[lane] = m_run;
-    xm[64 + lane] = l_run;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xo[(db * 16 + i) * 64 + lane] = o[db][i];
-  }
-  __syncthreads();
-  if (kh == 1 || qrow < 0) return;
-  const float m1 = xm[lane], l1 = xm[64 + lane];
-  const float m = fmaxf(m_run, m1);
-  const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
-  const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-  const float l = l_run * a0 + l1 * a1;
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (qrow < 0) return;
+  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   uint16_t *ob = static_cast<uint16_t *>(a.out) + int64_t(qrow) * a.out_stride_s +
                  int64_t(heads.h[hi]) * a.out_stride_h;
 #pragma unroll
@@ -421,11 +344,8 @@ __global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadL
       const int d = db * 32 + 8 * p + 4 * g;
       uint16_t h4[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float o1 = xo[(db * 16 + 4 * p + r) * 64 + lane];
-        const float v = (o[db][4 * p + r] * a0 + o1 * a1) * inv;
-        h4[r] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-      }
+      for (int r = 0; r < 4; ++r)
+        h4[r] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o[db][4 * p + r] * inv));
       uint2 w;
       w.x = uint32_t(h4[0]) | (uint32_t(h4[1]) << 16);
       w.y = uint32_t(h4[2]) | (uint32_t(h4[3]) << 16);
@@ -437,9 +357,9 @@ hipError_t launch_attend_bf16(const AttendArgs &a, const HeadList &heads, int he
                               hipStream_t s) {
   const dim3 grid(grid_blocks(a));
   if (head_dim == 128)
-    hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(512), 0, s, a, heads);
+    hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(256), 0, s, a, heads);
   else
-    hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(512), 0, s, a, heads);
+    hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(256), 0, s, a, heads);
   return hipGetLastError();
 }
 
