@@ -195,9 +195,13 @@ veda_status veda_select(const veda_plan_info *info, const veda_select_info *sel,
  *                 every row of the listed heads is written exactly once;
  *                 other heads are untouched.
  *   scale         softmax scale; <= 0 means head_dim^-1/2.
- * bf16 runs on MFMA (fp32 accumulate); f32 on the vector ALU. Errors:
- * UNSUPPORTED for head_dim not in {64, 128}, or bf16 pointers/strides not
- * 16-byte aligned. Asynchronous on `stream`. */
+ * Every CSR row lists at least one tile (veda_select's rows always do; an
+ * empty row leaves zeros). bf16 runs on MFMA (fp32 accumulate); f32 on the
+ * vector ALU. Errors: UNSUPPORTED for head_dim not in {64, 128}; for bf16,
+ * pointers/strides not 16-byte aligned, stride_s below head_dim or at least
+ * 2^23 elements, seq_len of 2^24 rows or more, or one head's rows spanning
+ * more than 3.5 GiB (rows are addressed with 32-bit offsets). Asynchronous
+ * on `stream`. */
 veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
                         const int32_t *perm, const int32_t *valid_count,
                         const void *q, const void *k, const void *v, void *out,

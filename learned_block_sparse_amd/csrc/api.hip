@@ -222,10 +222,14 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
   const int64_t kv_extent = ((info->seq_len - 1) * stride_s + D) * elt;
   if (dtype == VEDA_BF16 && kv_extent > int64_t(0xE0000000))
     return fail(VEDA_ERR_UNSUPPORTED, "q/k/v rows of one head span more than 3.5 GiB");
-  // Padding rows are read at offset (2^32 - row pitch + chunk), which must fall
-  // past the range above: rows may not overlap and the pitch stays modest.
-  if (dtype == VEDA_BF16 && (stride_s < D || stride_s * 2 > (int64_t(1) << 29)))
-    return fail(VEDA_ERR_UNSUPPORTED, "bf16 attend needs D <= stride_s <= 2^28 elements");
+  // Row offsets are formed as row * pitch + chunk with 24-bit factors; a
+  // padding slot is read as row seq_len, which must fall past the range above
+  // (rows may not overlap) and still fit in 32 bits.
+  if (dtype == VEDA_BF16 && (stride_s < D || stride_s * 2 >= (int64_t(1) << 24) ||
+                             info->seq_len >= (int64_t(1) << 24) ||
+                             (info->seq_len + 1) * stride_s * 2 > int64_t(0xFFFFFFFF)))
+    return fail(VEDA_ERR_UNSUPPORTED,
+                "bf16 attend needs D <= stride_s < 2^23 elements and seq_len < 2^24 rows");
   if (!(scale > 0.0f)) scale = float(1.0 / std::sqrt(double(D)));
   AttendArgs a;
   a.q = q;
@@ -245,6 +249,7 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
   a.n_tiles = info->n_tiles;
   a.n_video = info->n_video;
   a.kv_bytes = uint32_t(kv_extent);
+  a.pad_row = uint32_t(info->seq_len);
   a.scale = scale;
   a.scale_log2 = float(double(scale) * 1.4426950408889634);
   hipError_t e = dtype == VEDA_BF16 ? launch_attend_bf16(a, hl, D, stream)

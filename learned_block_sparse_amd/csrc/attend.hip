@@ -29,9 +29,9 @@ struct BlockMap {
   bool live;
 };
 
-__device__ inline BlockMap map_block(const AttendArgs &a, uint32_t b) {
+__device__ inline BlockMap map_block(const AttendArgs &a, int32_t n_units, uint32_t b) {
   BlockMap m{0, 0, false};
-  const uint32_t G = uint32_t(a.n_heads) * uint32_t(a.n_tiles - a.n_video);
+  const uint32_t G = uint32_t(n_units) * uint32_t(a.n_tiles - a.n_video);
   const uint32_t Gp = (G + 7u) & ~7u;
   if (b < Gp) {
     if (b >= G) return m;
@@ -42,7 +42,7 @@ __device__ inline BlockMap map_block(const AttendArgs &a, uint32_t b) {
     return m;
   }
   const uint32_t bv = b - Gp;
-  const uint32_t NV = uint32_t(a.n_heads) * uint32_t(a.n_video);
+  const uint32_t NV = uint32_t(n_units) * uint32_t(a.n_video);
   const uint32_t per = (NV + 7u) / 8u;
   const uint32_t logical = (bv % 8u) * per + bv / 8u;
   if (logical >= NV) return m;
@@ -52,22 +52,25 @@ __device__ inline BlockMap map_block(const AttendArgs &a, uint32_t b) {
   return m;
 }
 
-__host__ inline uint32_t grid_blocks(const AttendArgs &a) {
-  const uint32_t G = uint32_t(a.n_heads) * uint32_t(a.n_tiles - a.n_video);
+__host__ inline uint32_t grid_blocks(const AttendArgs &a, int32_t n_units) {
+  const uint32_t G = uint32_t(n_units) * uint32_t(a.n_tiles - a.n_video);
   const uint32_t Gp = (G + 7u) & ~7u;
-  const uint32_t NV = uint32_t(a.n_heads) * uint32_t(a.n_video);
+  const uint32_t NV = uint32_t(n_units) * uint32_t(a.n_video);
   return Gp + 8u * ((NV + 7u) / 8u);
 }
 
 // --------------------------------------------------------------- bf16 MFMA --
-// 4 wavefronts per workgroup, two workgroups per CU (one wave of each on
-// every SIMD): wave w takes query rows 32w .. 32w+31 and all 128 keys of
-// every kept tile, so each wave owns its rows' softmax state outright and no
-// merge is needed. The two workgroups keep their own barriers; their phases
-// drift apart, so one group's MFMAs overlap the other's softmax.
+// One workgroup of 8 wavefronts per CU, in two groups of 4 that take the same
+// query tile for a pair of heads (the tile lists of every head have the same
+// length, so both groups run the same number of steps). Within a group, wave
+// w takes query rows 32w .. 32w+31 and all 128 keys of every kept tile, so it
+// owns its rows' softmax state outright. Waves w and w+4 share a SIMD; the
+// groups run the same four half-phases per tile two half-phases apart, so on
+// every SIMD one group's MFMAs (S and P V) meet the other's vector work (the
+// softmax). Workgroup barriers close the half-phases and keep that offset.
 //
 // K and V tiles arrive in LDS by direct buffer-to-LDS loads (no register
-// staging) into one K and one V array per workgroup. Such a load writes 64
+// staging) into one K and one V array per group. Such a load writes 64
 // lanes x 16 bytes contiguously, so rows are stored unpadded and each
 // 16-byte chunk c of row r sits at chunk position c ^ swz(r), which keeps
 // both read patterns free of bank conflicts (64 banks):
@@ -81,9 +84,9 @@ __host__ inline uint32_t grid_blocks(const AttendArgs &a) {
 //      receives V[k0 + j][d0 + i] for j = 0..3: four keys of one column (swz
 //      gives the four rows of a read disjoint chunk positions).
 // Rows are fetched with 32-bit offsets from a per-head buffer descriptor; a
-// padding slot gets an offset past the descriptor's range, which the
-// hardware returns as zeros (the page's tile-ordered copies hold zeros in
-// padding slots).
+// padding slot is fetched as the row one past the last, outside the
+// descriptor's range, which the hardware returns as zeros (the page's
+// tile-ordered copies hold zeros in padding slots).
 template <int D>
 struct Bf16Cfg {
   static constexpr int ROW = D * 2;                          // bytes per row
@@ -107,9 +110,14 @@ __device__ inline int swz_v(int row) {
 __device__ inline uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+// Tile lists and valid counts are read with uniform indices and never written
+// by this kernel: reading them through the constant address space gives
+// scalar loads, which do not count against the vector-memory counter that
+// the load pipeline's waits rely on.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ inline const_i32 *as_const(const int32_t *p) { return (const_i32 *)(p); }
 
 // Exchange with the lane 32 apart through v_permlane32_swap (VALU; no LDS
 // round trip): with both operands x, the two results hold x from each half,
@@ -129,15 +137,36 @@ __device__ inline s16x4 ds_read_tr(const unsigned char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
 }
 
-template <int D>
-__global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadList heads) {
+template <int N>
+__device__ inline void barrier_vm() {
+  // this wave's loads older than the newest N have landed, its LDS reads have
+  // returned; then the workgroup barrier
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ inline void barrier_lds() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One group (4 waves) of the ping-pong workgroup; GROUP selects its LDS
+// buffers and its place in the schedule.
+template <int D, int GROUP>
+__device__ __attribute__((always_inline)) inline void attend_group(const AttendArgs &a,
+                                                                   const HeadList &heads,
+                                                                   int32_t pair, int32_t tile,
+                                                                   int wave) {
   using C = Bf16Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char Kb[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char Vb[C::TILE_BYTES];
 
-  const BlockMap bm = map_block(a, blockIdx.x);
-  if (!bm.live) return;
-  const int hi = bm.hi, tile = bm.tile;
+  // The second group of the last pair of an odd head count repeats the first
+  // group's head (it keeps the schedule) and writes nothing.
+  const int32_t hi_raw = 2 * pair + GROUP;
+  const bool shadow = hi_raw >= a.n_heads;
+  const int32_t hi = shadow ? hi_raw - 1 : hi_raw;
   const int64_t hoff = int64_t(heads.h[hi]) * a.stride_h;
   const uint16_t *qb = static_cast<const uint16_t *>(a.q) + hoff;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -146,9 +175,7 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
       const_cast<uint16_t *>(static_cast<const uint16_t *>(a.v) + hoff), 0, int(a.kv_bytes), 0x00020000);
   const uint32_t row_bytes = uint32_t(a.stride_s) * 2u;
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // scalar: LDS bases stay in SGPRs
-  const int lane = tid % 64;
+  const int lane = threadIdx.x % 64;
   const int g = lane / 32, l32 = lane % 32;
 
   // Q fragment (B operand of S^T = K Q^T): q[row][16*ks + 8*g .. +8]
@@ -171,11 +198,12 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int32_t t_begin = a.row_offsets[tile], t_end = a.row_offsets[tile + 1];
-  const int32_t *list = a.cols + int64_t(hi) * a.entries_per_head;
+  const const_i32 *list = as_const(a.cols + int64_t(hi) * a.entries_per_head);
+  const const_i32 *vcount = as_const(a.valid_count);
   const int n_t = t_end - t_begin;
 
-  // Load mapping: wave w fills rows 32w .. 32w+31 of a tile with 2*LOADS
-  // direct loads per tensor; load i lands at bytes (32w + R*i)*ROW + 16*lane
+  // Load mapping: wave w fills rows 32w .. 32w+31 of a tile with NL direct
+  // loads per tensor; load i lands at bytes (32w + R*i)*ROW + 16*lane
   // (R = rows per load), i.e. row 32w + R*i + lane/CHUNKS, chunk position
   // lane%CHUNKS, which holds global chunk position ^ swz(row).
   constexpr int NL = 2 * C::LOADS;
@@ -190,6 +218,7 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
   struct Rows {
     int32_t r[NL];
   };
+  auto list_at = [&](int idx) -> int32_t { return list[t_begin + min(idx, n_t - 1)]; };
   auto rows_of = [&](int32_t j) {
     Rows out;
     const int32_t *pj = a.perm + int64_t(j) * VEDA_TILE + 32 * wave + ld_row;
@@ -197,24 +226,25 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
     for (int i = 0; i < NL; ++i) out.r[i] = pj[C::ROWS_PER_LOAD * i];
     return out;
   };
-  // A padding row (id -1) gives 2^32 - row_bytes + chunk, past the
-  // descriptor's range (the host keeps row_bytes <= 2^29, every chunk below
-  // row_bytes and the range below 0xE0000000), so it reads as zeros.
-  auto dma = [&](const __amdgpu_buffer_rsrc_t &rsrc, unsigned char *dst, const Rows &rows,
-                 const uint32_t (&chunk)[NL]) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const uint32_t off = uint32_t(rows.r[i]) * row_bytes + chunk[i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (lds_void *)(dst + (32 * wave + C::ROWS_PER_LOAD * i) * C::ROW), 16, off, 0, 0, 0);
-    }
+  // A padding row (id -1) is clamped to seq_len, one row past the end: its
+  // offset is past the descriptor's range (the host keeps seq_len and the
+  // row pitch below 2^24, so the 24-bit product is exact), so it reads as
+  // zeros.
+  auto dma1 = [&](const __amdgpu_buffer_rsrc_t &rsrc, unsigned char *dst, int32_t row, int i,
+                  uint32_t chunk) {
+    const uint32_t r = min(uint32_t(row), a.pad_row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (lds_void *)(dst + (32 * wave + C::ROWS_PER_LOAD * i) * C::ROW), 16,
+        __umul24(r, row_bytes) + chunk, 0, 0, 0);
   };
 
   // Compute-side read offsets (per lane; swizzled positions).
   const uint32_t k_sw = uint32_t(swz_k<D>(l32));
-  uint32_t k_off[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = uint32_t(l32 * C::ROW) + 16u * ((uint32_t(2 * ks + g)) ^ k_sw);
+  // chunk (2ks + g) ^ k_sw = 2 (ks ^ (k_sw >> 1)) + (g ^ (k_sw & 1)): one
+  // xor-add per k step instead of KS live registers
+  const uint32_t k_base = uint32_t(l32 * C::ROW) + 16u * (uint32_t(g) ^ (k_sw & 1u));
+  const uint32_t k_h32 = 32u * (k_sw >> 1);
+  auto k_off = [&](int ks) -> uint32_t { return k_base + ((32u * uint32_t(ks)) ^ k_h32); };
   const int G = lane >> 4, s16 = lane & 15;
   const int vrow = 4 * (G >> 1) + (s16 >> 2);
   const int vcol = 16 * (G & 1) + 4 * (s16 & 3);
@@ -225,26 +255,41 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
     v_off[db] = uint32_t(vrow * C::ROW) + 16u * uint32_t((d >> 3) ^ swz_v<D>(vrow)) + 8u * ((d >> 2) & 1);
   }
 
-  auto list_at = [&](int idx) -> int32_t { return list[t_begin + min(idx, n_t - 1)]; };
-
-  // Per tile: S(t) from K -> barrier, start K(t+1) -> softmax(t) -> P(t)V(t)
-  // from V -> barrier, start V(t+1). Each barrier also waits for the loads
-  // started at the previous one, so K(t+1) has the softmax and P V phases to
-  // land and V(t+1) the next S and softmax phases. Two workgroups share a CU
-  // and keep their own barriers, so their phases drift apart and one group's
-  // MFMAs overlap the other's vector work.
-  Rows rows_next = rows_of(list_at(1));
-  {
-    const Rows rows0 = rows_of(list_at(0));
-    dma(rk, Kb, rows0, k_chunk);
-    dma(rv, Vb, rows0, v_chunk);
-  }
-  int32_t j2 = list_at(2);
-  int32_t vc_cur = a.valid_count[list_at(0)], vc_next = a.valid_count[list_at(1)];
-  __syncthreads();
-
-  for (int t = 0; t < n_t; ++t) {
-    f32x16 s[4];
+  f32x16 s[4];
+  bf16x8 pb[4][2];
+  // S^T = K Q^T for the key tile in Kb, the reads of each k step issued one
+  // step ahead of its MFMAs; the V loads of `rows` (NL of them) are spread
+  // over the k steps, between the MFMAs, so no wave waits on the address
+  // unit's queue.
+  auto scores_with_v = [&](const Rows &rows) {
+    bf16x8 A[2][4];
+    auto read_k = [&](int ks, bf16x8 (&dst)[4]) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        dst[kb] = *reinterpret_cast<const bf16x8 *>(Kb + k_off(ks) + kb * 32 * C::ROW);
+    };
+    read_k(0, A[0]);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (ks + 1 < C::KS) read_k(ks + 1, A[(ks + 1) & 1]);
+      if (ks % (C::KS / NL) == 0) {
+        const int i = ks / (C::KS / NL);
+        dma1(rv, Vb, rows.r[i], i, v_chunk[i]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks & 1][kb], qf[ks], ks == 0 ? f32x16{} : s[kb],
+                                                        0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (ks + 1 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if (ks % (C::KS / NL) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+  };
+  auto scores = [&]() {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -253,22 +298,89 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8 *>(Kb + k_off[ks] + kb * 32 * C::ROW);
+        const bf16x8 A = *reinterpret_cast<const bf16x8 *>(Kb + k_off(ks) + kb * 32 * C::ROW);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[ks], s[kb], 0, 0, 0);
       }
-    __syncthreads();   // every wave is done with K(t); V(t) has landed
-    // no load may still be writing LDS when the workgroup ends: the last
-    // tile starts none
-    const bool more = t + 1 < n_t;
-    if (more) dma(rk, Kb, rows_next, k_chunk);
-    const Rows rows_v = rows_next;
-    rows_next = rows_of(j2);
-    const int32_t vc_new = a.valid_count[j2];
-    j2 = list_at(t + 3);
+  };
+  // probabilities of keys 8h .. 8h+7 of block kb (in the S^T layout)
+  float racc[4];   // this tile's row sum, four partial sums
+  auto exps8 = [&](int kb, int h) {
+#pragma unroll
+    for (int i = 8 * h; i < 8 * h + 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_run));
+      pb[kb][h][i % 8] = static_cast<__bf16>(p);
+      racc[i & 3] += p;
+    }
+  };
+  // Lazy rescale: takes the running max to mx (log2 units) only when mx
+  // exceeds it by more than 8, so probabilities stay <= 256 (exact range in
+  // fp32 and bf16), and scales O and the row sum to match.
+  auto rescale = [&](float mx) {
+    if (mx > m_run + 8.0f) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+      m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+  };
 
+  // Schedule. Each group's work per kept tile t is cut into four
+  // half-phases, each closed by a workgroup barrier:
+  //   A: softmax(t) first part (mask, max, rescale, probabilities of keys
+  //      0..31), loads of K(t+1) spread through it
+  //   B: softmax(t) rest (probabilities of keys 32..127, row sum)
+  //   C: P(t) V(t)
+  //   D: S(t+1) = K(t+1) Q^T, loads of V(t+1) spread through it
+  // The two groups run two half-phases apart (the group on waves 0-3 behind),
+  // so A and B of one group meet C and D of the other. K(t+1) has B and C
+  // to land, V(t+1) has A and B. Every load is issued unconditionally (past
+  // the end of the list the last tile is fetched again), so the barriers can
+  // wait with exact counts: in issue order come the row ids of tile t+1
+  // (in D), V(t) (in D), K(t+1) (in A), the row ids of tile t+1 again (in C),
+  // NL loads each; V(t) is waited for at the end of B with K(t+1) still
+  // allowed in flight, K(t+1) at the end of C with those row ids in flight.
+  // The prologue keeps the same order (row ids of tile 1 before V(0)), so the
+  // compiler's own waits for the row ids agree on the first and later tiles.
+  // Both groups see the same list length (the same tile): an empty list,
+  // which veda_select never produces, skips the loop in both alike and
+  // leaves zeros.
+  if (n_t > 0) {
+  Rows Rk;
+  {
+    const Rows R0 = rows_of(list_at(0));
+#pragma unroll
+    for (int i = 0; i < NL; ++i) dma1(rk, Kb, R0.r[i], i, k_chunk[i]);
+    asm volatile("" ::: "memory");
+    Rk = rows_of(list_at(1));
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NL; ++i) dma1(rv, Vb, R0.r[i], i, v_chunk[i]);
+  }
+  if constexpr (GROUP == 0) {
+    barrier_vm<0>();
+    scores();
+    barrier_lds();
+  } else {
+    barrier_lds();
+    barrier_lds();
+    barrier_vm<0>();
+    scores();
+    barrier_lds();
+  }
+  int32_t vc_cur = vcount[list_at(0)];
+
+  for (int t = 0; t < n_t; ++t) {
+    const int32_t vc_next = vcount[list_at(t + 1)];
+    __builtin_amdgcn_s_setprio(0);   // vector half-phases yield to the other group's MFMAs
+    // ---- A
     if (vc_cur < VEDA_TILE) {
       asm volatile("" ::: "memory");
-      const int thr = vc_cur - 4 * g;
+      // lane group from the lane id, recomputed here rather than kept live
+      const int g4 = int(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5) * 4;
+      const int thr = vc_cur - g4;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -280,60 +392,82 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = pair_max(mx) * a.scale_log2;
-    // Lazy rescale: keep the running max unless this tile exceeds it by more
-    // than 2^8; probabilities then stay <= 256, exact in fp32 and bf16 range.
-    if (mx > m_run + 8.0f) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
-      m_run = mx;
-      l_run *= alpha;
+    rescale(pair_max(mx) * a.scale_log2);
+    racc[0] = racc[1] = racc[2] = racc[3] = 0.0f;
+    // K(t+1) streams in between chunks of probabilities, a few loads at a
+    // time, so no wave waits on the address unit's queue.
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      for (int i = c * NL / 2; i < (c + 1) * NL / 2; ++i) dma1(rk, Kb, Rk.r[i], i, k_chunk[i]);
+      __builtin_amdgcn_sched_barrier(0);
+      exps8(0, c);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    bf16x8 pb[4][2];
+    barrier_lds();
+    // ---- B
+    exps8(1, 0);
+    exps8(1, 1);
+    exps8(2, 0);
+    exps8(2, 1);
+    exps8(3, 0);
+    exps8(3, 1);
+    l_run += pair_sum((racc[0] + racc[1]) + (racc[2] + racc[3]));
+    barrier_vm<NL>();   // V(t) landed in every wave (K(t+1) may not)
+    const Rows Rv = rows_of(list_at(t + 1));
+    __builtin_amdgcn_s_setprio(1);   // MFMA half-phases issue first
+    // ---- C
+    // P(t) V(t), the V^T fragments of each k step read one step ahead
+    {
+      s16x4 Vf[2][C::DB][2];
+      auto read_v = [&](int kstep, s16x4 (&dst)[C::DB][2]) {
+        const int kb = kstep >> 1, e = kstep & 1;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_run));
-        pb[kb][i / 8][i % 8] = static_cast<__bf16>(p);
-      }
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float rs = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const bf16x2 pr = {pb[kb][e][2 * q2], pb[kb][e][2 * q2 + 1]};
-          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+        for (int db = 0; db < C::DB; ++db) {
+          const unsigned char *p0 = Vb + v_off[db] + (kb * 32 + e * 16) * C::ROW;
+          dst[db][0] = ds_read_tr(p0);
+          dst[db][1] = ds_read_tr(p0 + 8 * C::ROW);
         }
-    l_run += pair_sum(rs);
-
+      };
+      read_v(0, Vf[0]);
 #pragma unroll
-    for (int kstep = 0; kstep < 8; ++kstep) {
-      const int kb = kstep >> 1, e = kstep & 1;
+      for (int kstep = 0; kstep < 8; ++kstep) {
+        if (kstep + 1 < 8) read_v(kstep + 1, Vf[(kstep + 1) & 1]);
+        const int kb = kstep >> 1, e = kstep & 1;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const unsigned char *p0 = Vb + v_off[db] + (kb * 32 + e * 16) * C::ROW;
-        const s16x4 lo = ds_read_tr(p0);
-        const s16x4 hi4 = ds_read_tr(p0 + 8 * C::ROW);
-        const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
-                                                              hi4[0], hi4[1], hi4[2], hi4[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[kb][e],
-                                                       o[db], 0, 0, 0);
+        for (int db = 0; db < C::DB; ++db) {
+          const s16x4 lo = Vf[kstep & 1][db][0], hi4 = Vf[kstep & 1][db][1];
+          const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
+                                                                hi4[0], hi4[1], hi4[2], hi4[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8),
+                                                         pb[kb][e], o[db], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DB, 0);
+#pragma unroll
+      for (int kstep = 0; kstep < 8; ++kstep) {
+        if (kstep + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::DB, 0);
       }
     }
-    __syncthreads();   // every wave is done with V(t); K(t+1) has landed
-    if (more) dma(rv, Vb, rows_v, v_chunk);
+    barrier_vm<NL>();   // K(t+1) landed; every wave is done with V(t)
+    // ---- D
+    Rk = rows_of(list_at(t + 2));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    scores_with_v(Rv);
+    barrier_lds();     // every wave is done with K(t+1)
     vc_cur = vc_next;
-    vc_next = vc_new;
+  }
+  if constexpr (GROUP == 0) {
+    barrier_lds();
+    barrier_lds();
+  }
+  // the loads past the end of the list must land before the LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
-  if (qrow < 0) return;
+  if (qrow < 0 || shadow) return;
   const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   uint16_t *ob = static_cast<uint16_t *>(a.out) + int64_t(qrow) * a.out_stride_s +
                  int64_t(heads.h[hi]) * a.out_stride_h;
@@ -353,13 +487,26 @@ __global__ void __launch_bounds__(256, 2) attend_bf16_kernel(AttendArgs a, HeadL
     }
 }
 
+template <int D>
+__global__ void __launch_bounds__(512, 1) attend_bf16_kernel(AttendArgs a, HeadList heads) {
+  const int32_t n_pairs = (a.n_heads + 1) / 2;
+  const BlockMap bm = map_block(a, n_pairs, blockIdx.x);
+  if (!bm.live) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);   // scalar
+  // the leading schedule on waves 4-7 measured faster than on waves 0-3
+  if (wave >= 4)
+    attend_group<D, 0>(a, heads, bm.hi, bm.tile, wave - 4);
+  else
+    attend_group<D, 1>(a, heads, bm.hi, bm.tile, wave);
+}
+
 hipError_t launch_attend_bf16(const AttendArgs &a, const HeadList &heads, int head_dim,
                               hipStream_t s) {
-  const dim3 grid(grid_blocks(a));
+  const dim3 grid(grid_blocks(a, (a.n_heads + 1) / 2));
   if (head_dim == 128)
-    hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(256), 0, s, a, heads);
+    hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(512), 0, s, a, heads);
   else
-    hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(256), 0, s, a, heads);
+    hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(512), 0, s, a, heads);
   return hipGetLastError();
 }
 
@@ -371,7 +518,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendArgs a, HeadList 
   constexpr int HD = D / 2;
   __shared__ float ks[F32_CHUNK][D + 4];
   __shared__ float vs[F32_CHUNK][D + 4];
-  const BlockMap bm = map_block(a, blockIdx.x);
+  const BlockMap bm = map_block(a, a.n_heads, blockIdx.x);
   if (!bm.live) return;
   const int hi = bm.hi, tile = bm.tile;
   const int64_t hoff = int64_t(heads.h[hi]) * a.stride_h;
@@ -448,7 +595,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendArgs a, HeadList 
 
 hipError_t launch_attend_f32(const AttendArgs &a, const HeadList &heads, int head_dim,
                              hipStream_t s) {
-  const dim3 grid(grid_blocks(a));
+  const dim3 grid(grid_blocks(a, a.n_heads));
   if (head_dim == 128)
     hipLaunchKernelGGL(attend_f32_kernel<128>, grid, dim3(256), 0, s, a, heads);
   else

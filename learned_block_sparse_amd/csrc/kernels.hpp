@@ -80,6 +80,7 @@ struct AttendArgs {
   int64_t entries_per_head;
   int32_t n_heads, n_tiles, n_video;
   uint32_t kv_bytes;         // bytes from a head's first K/V element to the end of its last row
+  uint32_t pad_row;          // a padding slot (row id -1) is fetched as this row, one past the last
   float scale_log2;          // softmax scale * log2(e)
   float scale;               // softmax scale
 };

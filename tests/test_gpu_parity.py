@@ -179,15 +179,17 @@ def test_keep_all_equals_dense_attention():
         assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
 
 
-def test_head_subset_leaves_other_heads_untouched():
+@pytest.mark.parametrize("sub", [[1, 3], [0, 2, 3], [2]])
+def test_head_subset_leaves_other_heads_untouched(sub):
+    """Even and odd head counts (heads are processed in pairs on the bf16 path)."""
     inp, dev, groups = _make("padding")
     g = groups[0]
     out = torch.full_like(dev["q"], 7.0)
-    sub = [1, 3]
+    rest = [h for h in range(inp.q.shape[1]) if h not in sub]
     gg = GpuGroup(inp, dev, g.shape, sub)
     gg.attend(dev, out=out)
     o = out.float().cpu().numpy()
-    assert (o[:, [0, 2]] == 7.0).all()
+    assert (o[:, rest] == 7.0).all()
     kept = selection.select(predictor.logits(
         predictor.pool(inp.q, g.layout, sub), predictor.pool(inp.k, g.layout, sub),
         inp.proj_q[sub], inp.proj_k[sub]), g.layout, g.blocks)

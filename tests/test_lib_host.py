@@ -160,3 +160,26 @@ def test_select_query_unsupported_head_dim():
     info = veda.veda_plan_query([(0, (4, 16, 16), None)], 1024)
     with pytest.raises(veda.VedaUnsupported):
         veda.veda_select_query(info, veda.budget(("ratio", 0.2)), veda.budget(("ratio", 0.2)), 96, 1)
+
+
+@pytest.mark.parametrize("grid,seq_len,D,stride_s", [
+    ((64, 512, 512), 1 << 24, 64, 64),    # 2^24 rows (2 GiB): past the 24-bit row factor
+    ((1, 1, 1), 1, 128, 1 << 23),         # row pitch of 2^24 bytes (one row: tiny extent)
+    ((4, 16, 16), 4096, 128, 64),         # rows narrower than head_dim overlap
+])
+def test_attend_refuses_unaddressable_bf16_rows(grid, seq_len, D, stride_s):
+    """The bf16 path forms row offsets as 24-bit row x 24-bit pitch in 32 bits;
+    layouts outside that are refused before any device work (dummy aligned
+    pointers are never dereferenced on this path)."""
+    import ctypes as C
+    from learned_block_sparse_amd import _lib
+    lib = _lib.load()
+    info = veda.veda_plan_query([(0, grid, None)], seq_len)
+    sel = veda.veda_select_query(info, veda.budget(("tiles", 1.0)), veda.budget(("tiles", 1.0)),
+                                 D, 1)
+    heads = (C.c_int32 * 1)(0)
+    dummy = C.c_void_p(1 << 20)
+    st = lib.veda_attend(C.byref(info), C.byref(sel), dummy, dummy, dummy, dummy, dummy, dummy,
+                         1, stride_s, D, stride_s, D, 1, heads, dummy, dummy, 0.0, None)
+    assert st == 2
+    assert "bf16 attend needs" in lib.veda_last_error().decode()
