@@ -38,7 +38,56 @@ def _args():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run two device copies of MIB MiB (the known-size kernel that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+# HBM traffic of the attend kernel, from rocprofv3 counter runs recorded in
+# this file (see it for the commands and the copy-kernel calibration). It is
+# reported only while the kernel source is the one the counters were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_headline_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "learned_block_sparse_amd", "csrc", n)
+                  for n in ("attend.hip", "kernels.hpp")]
+
+
+def _kernel_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _recorded_traffic(workload):
+    """Bytes per attend launch from the recorded counters, or None when the
+    record is missing, for another workload, or for another kernel source."""
+    import re
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"<!-- traffic (\{.*?\}) -->", text)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("workload") != workload or rec.get("kernel_sha256") != _kernel_digest():
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+def _copy_probe(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 2}), flush=True)
 
 
 def _log(msg):
@@ -168,6 +217,9 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        _copy_probe(args.copy_probe)
+        return
     _log(f"[bench] generating {args.workload}")
     inp = workloads.generate(args.workload)
     wl = inp.workload
@@ -243,7 +295,8 @@ def main():
         "attend_pct_bf16_peak": 100.0 * attend_tflops / BF16_PEAK_TFLOPS,
         "roofline": {
             "bound": "mfma", "achieved": attend_tflops, "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": attend_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": attend_tflops / BF16_PEAK_TFLOPS,
+            "traffic": _recorded_traffic(wl.name),
         },
         "cpu_baseline": None,
     }
