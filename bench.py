@@ -10,6 +10,8 @@ stream the kernels run on. Prints one JSON line:
   ms_per_step  ms per layer (plan + select + attend)
   roofline     the attend kernel against MI355X's dense bf16 MFMA peak
   cpu_baseline the CPU oracle on a bounded sample of the same layer, scaled
+plus context: attend TFLOP/s over real rows only, and the vendor library's
+bf16 GEMM rate measured in the same run (the practical MFMA ceiling).
 """
 from __future__ import annotations
 
@@ -139,6 +141,22 @@ class Layer:
         self.pairs = sum(len(g["heads"]) * g["sel"].entries_per_head for g in self.groups)
         self.flops = self.pairs * 4.0 * 128 * 128 * wl.head_dim
 
+    def real_row_flops(self):
+        """Flops over real rows only: sum over kept pairs (a, b) of
+        4 * D * valid_count[a] * valid_count[b] (call after select)."""
+        import torch
+        total = 0.0
+        for g in self.groups:
+            vc = g["vc"].double()
+            ro = g["ro"].long()
+            counts = ro[1:] - ro[:-1]
+            row_of_entry = torch.repeat_interleave(torch.arange(len(counts), device=vc.device),
+                                                   counts)
+            cols = g["cols"].view(len(g["heads"]), -1).long()
+            per_head = (vc[row_of_entry][None, :] * vc[cols]).sum()
+            total += float(per_head) * 4.0 * self.wl.head_dim
+        return total
+
     def plan(self):
         for g in self.groups:
             self.veda.veda_plan(g["info"], g["perm"], g["vc"])
@@ -155,6 +173,35 @@ class Layer:
         for g in self.groups:
             v.veda_attend(g["info"], g["sel"], g["perm"], g["vc"], self.t["q"], self.t["k"],
                           self.t["v"], g["heads"], g["ro"], g["cols"], out=self.out)
+
+
+def _gemm_ceiling(n=16384, reps=5):
+    """bf16 dense GEMM rate of the vendor library on this GPU (n x n x n,
+    fp32 accumulate), the practical MFMA ceiling beside the published peak."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _cpu_baseline(inp, layer_pairs, head_dim, seconds):
@@ -200,6 +247,7 @@ def _cpu_baseline(inp, layer_pairs, head_dim, seconds):
     flops = layer_pairs * 4.0 * 128 * 128 * head_dim
     return {
         "value": flops / est / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "cpu_model": _cpu_model(),
         "sample": (f"head 0 of {wl.n_heads}: plan + pool + logits + select ({t_sel:.2f} s), then "
                    f"exact fp64 attention for {n_tiles} query tiles ({done_pairs} kept pairs, "
                    f"{t_att:.2f} s); layer time extrapolated to {est:.1f} s"),
@@ -263,6 +311,9 @@ def main():
          f"{np.median(sel_ms):.3f} attend {np.median(att_ms):.3f}")
 
     attend_tflops = L.flops / (att_avg * 1e-3) / 1e12
+    real_flops = L.real_row_flops()
+    gemm = _gemm_ceiling()
+    _log(f"[bench] bf16 GEMM ceiling {gemm:.1f} TFLOP/s")
     result = {
         "metric": METRIC,
         "value": L.flops / (ms_step * 1e-3) / 1e12,
@@ -293,6 +344,9 @@ def main():
         },
         "attend_tflops": attend_tflops,
         "attend_pct_bf16_peak": 100.0 * attend_tflops / BF16_PEAK_TFLOPS,
+        "attend_real_row_tflops": real_flops / (att_avg * 1e-3) / 1e12,
+        "gemm_ceiling_tflops": gemm,
+        "attend_pct_gemm_ceiling": 100.0 * attend_tflops / gemm,
         "roofline": {
             "bound": "mfma", "achieved": attend_tflops, "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": attend_tflops / BF16_PEAK_TFLOPS,
