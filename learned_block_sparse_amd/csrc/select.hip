@@ -77,87 +77,113 @@ hipError_t launch_pool(const PoolArgs &a, const HeadList &heads, const int32_t *
 }
 
 // --------------------------------------------------------------- project --
-constexpr int PROJ_TILES = 16;
+// fp64 GEMM C = A B for the two small products of the predictor (about 4 and
+// 5 GFLOP at the headline): a 64 x 64 output tile per 256-thread block, K in
+// steps of 16 staged in LDS k-major, each thread a 4 x 4 register tile whose
+// four A and four B values are contiguous (two 16-byte LDS reads each).
+constexpr int GT = 64, GK = 16;
 
-template <int D>
-__global__ void __launch_bounds__(D) project_kernel(ProjectArgs a) {
-  __shared__ double f[PROJ_TILES][3 * D];
-  const int t0 = blockIdx.x * PROJ_TILES;
-  const int hi = blockIdx.y;
-  const int which = blockIdx.z;
-  const int d = threadIdx.x;
-  const int nt = min(PROJ_TILES, a.n_video - t0);
-  const double *src = a.feat + ((int64_t(which) * a.n_heads + hi) * a.n_video + t0) * (3 * D);
-  for (int i = threadIdx.x; i < nt * 3 * D; i += D) f[i / (3 * D)][i % (3 * D)] = src[i];
-  __syncthreads();
-  double acc[PROJ_TILES];
+struct GemmTile {
+  double acc[4][4];
+};
+
+// A: [M][K] fp64 row-major. B element (k, n) from load_b(k, n); B_NK says
+// B is stored n-major ([N][K], loaded k-fastest like A) rather than k-major.
+template <bool B_NK, class LoadB>
+__device__ inline void gemm_tile(const double *A, int M, int K, int i0, int j0, int N,
+                                 LoadB load_b, GemmTile &t) {
+  // rows padded to 66 doubles (528 B, still 16-byte aligned): the k-fastest
+  // stores of 16 lanes then land in distinct banks
+  __shared__ __attribute__((aligned(16))) double As[GK][GT + 2];
+  __shared__ __attribute__((aligned(16))) double Bs[GK][GT + 2];
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
 #pragma unroll
-  for (int t = 0; t < PROJ_TILES; ++t) acc[t] = 0.0;
-  const float *P = a.proj[which] + int64_t(hi) * (3 * D) * D;
-  for (int e = 0; e < 3 * D; ++e) {
-    const double p = double(P[int64_t(e) * D + d]);
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int t = 0; t < PROJ_TILES; ++t) acc[t] = fma(f[t][e], p, acc[t]);
+    for (int w = 0; w < 4; ++w) t.acc[u][w] = 0.0;
+  for (int k0 = 0; k0 < K; k0 += GK) {
+    for (int idx = threadIdx.x; idx < GT * GK; idx += 256) {
+      const int r = idx / GK, kk = idx % GK;   // A: 16 consecutive k of one row
+      As[kk][r] = (i0 + r < M && k0 + kk < K) ? A[int64_t(i0 + r) * K + k0 + kk] : 0.0;
+      if constexpr (B_NK) {
+        Bs[kk][r] = (j0 + r < N && k0 + kk < K) ? load_b(k0 + kk, j0 + r) : 0.0;
+      } else {
+        const int kb = idx / GT, c = idx % GT;    // B: 64 consecutive n of one k
+        Bs[kb][c] = (j0 + c < N && k0 + kb < K) ? load_b(k0 + kb, j0 + c) : 0.0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < GK; ++kk) {
+      const double2 a01 = *reinterpret_cast<const double2 *>(&As[kk][ty * 4]);
+      const double2 a23 = *reinterpret_cast<const double2 *>(&As[kk][ty * 4 + 2]);
+      const double2 b01 = *reinterpret_cast<const double2 *>(&Bs[kk][tx * 4]);
+      const double2 b23 = *reinterpret_cast<const double2 *>(&Bs[kk][tx * 4 + 2]);
+      const double av[4] = {a01.x, a01.y, a23.x, a23.y};
+      const double bv[4] = {b01.x, b01.y, b23.x, b23.y};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) t.acc[u][w] = fma(av[u], bv[w], t.acc[u][w]);
+    }
+    __syncthreads();
   }
-  double *dst = a.out + ((int64_t(which) * a.n_heads + hi) * a.n_video + t0) * D;
-  for (int t = 0; t < nt; ++t) dst[int64_t(t) * D + d] = acc[t] + f[t][d];
+}
+
+// Projection (page `veda_core.py`, § predictor, `logits`): x_hat = f P + mean,
+// f = [mean | max | min] (3D wide), P [3D][D] per head; the mean is the first
+// D features of f.
+__global__ void __launch_bounds__(256) project_kernel(ProjectArgs a) {
+  const int D = a.head_dim, K = 3 * D, nv = a.n_video;
+  const int hi = blockIdx.z >> 1, which = blockIdx.z & 1;
+  const int i0 = blockIdx.y * GT, j0 = blockIdx.x * GT;
+  const double *F = a.feat + (int64_t(which) * a.n_heads + hi) * nv * K;
+  const float *P = a.proj[which] + int64_t(hi) * K * D;
+  GemmTile t;
+  gemm_tile<false>(F, nv, K, i0, j0, D, [&](int k, int n) { return double(P[int64_t(k) * D + n]); }, t);
+  double *dst = a.out + (int64_t(which) * a.n_heads + hi) * nv * D;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = i0 + ty * 4 + u;
+    if (i >= nv) continue;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int j = j0 + tx * 4 + w;
+      if (j < D) dst[int64_t(i) * D + j] = t.acc[u][w] + F[int64_t(i) * K + j];
+    }
+  }
 }
 
 hipError_t launch_project(const ProjectArgs &a, hipStream_t s) {
-  dim3 grid((a.n_video + PROJ_TILES - 1) / PROJ_TILES, a.n_heads, 2);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(project_kernel<128>, grid, dim3(128), 0, s, a);
-  else
-    hipLaunchKernelGGL(project_kernel<64>, grid, dim3(64), 0, s, a);
+  const dim3 grid((a.head_dim + GT - 1) / GT, (a.n_video + GT - 1) / GT, 2 * a.n_heads);
+  hipLaunchKernelGGL(project_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- scores --
-constexpr int SC_TILE = 64, SC_K = 16;
-
+// Logits (page `veda_core.py`, § predictor, `logits`): q_hat . k_hat / sqrt(D)
+// for every pair of video tiles, per head.
 __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a) {
-  __shared__ double As[SC_K][SC_TILE + 1];
-  __shared__ double Bs[SC_K][SC_TILE + 1];
   const int hi = blockIdx.z;
-  const int i0 = blockIdx.y * SC_TILE, j0 = blockIdx.x * SC_TILE;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int i0 = blockIdx.y * GT, j0 = blockIdx.x * GT;
   const int nv = a.n_video, D = a.head_dim;
   const double *A = a.qh + int64_t(hi) * nv * D;
   const double *B = a.kh + int64_t(hi) * nv * D;
-  double acc[4][4] = {};
-  for (int k0 = 0; k0 < D; k0 += SC_K) {
-    for (int idx = threadIdx.x; idx < SC_TILE * SC_K; idx += 256) {
-      const int r = idx / SC_K, kk = idx % SC_K;
-      As[kk][r] = (i0 + r < nv) ? A[int64_t(i0 + r) * D + k0 + kk] : 0.0;
-      Bs[kk][r] = (j0 + r < nv) ? B[int64_t(j0 + r) * D + k0 + kk] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < SC_K; ++kk) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        av[u] = As[kk][ty + 16 * u];
-        bv[u] = Bs[kk][tx + 16 * u];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fma(av[u], bv[w], acc[u][w]);
-    }
-    __syncthreads();
-  }
+  GemmTile t;
+  gemm_tile<true>(A, nv, D, i0, j0, nv, [&](int k, int n) { return B[int64_t(n) * D + k]; }, t);
   double *C = a.scores + int64_t(hi) * nv * nv;
   double *C2 = a.scores_copy ? a.scores_copy + int64_t(hi) * nv * nv : nullptr;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int i = i0 + ty + 16 * u;
+    const int i = i0 + ty * 4 + u;
     if (i >= nv) continue;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int j = j0 + tx + 16 * w;
+      const int j = j0 + tx * 4 + w;
       if (j >= nv) continue;
-      const double v = acc[u][w] / a.sqrt_d;
+      const double v = t.acc[u][w] / a.sqrt_d;
       C[int64_t(i) * nv + j] = v;
       if (C2) C2[int64_t(i) * nv + j] = v;
     }
@@ -165,7 +191,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a) {
 }
 
 hipError_t launch_scores(const ScoreArgs &a, hipStream_t s) {
-  const int nb = (a.n_video + SC_TILE - 1) / SC_TILE;
+  const int nb = (a.n_video + GT - 1) / GT;
   hipLaunchKernelGGL(score_kernel, dim3(nb, nb, a.n_heads), dim3(256), 0, s, a);
   return hipGetLastError();
 }
