@@ -16,7 +16,7 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import Budget, PlanInfo, SelectInfo, Span, TILE
 
-__all__ = ["VedaError", "VedaUnsupported", "VedaDeviceError", "budget", "veda_plan_query",
+__all__ = ["VedaError", "VedaUnsupported", "VedaDeviceError", "budget", "summary", "veda_plan_query",
            "veda_plan", "veda_select_query", "veda_select", "veda_attend", "Plan", "plan",
            "attention", "version", "library_path"]
 
@@ -226,7 +226,7 @@ def _head_groups(head_shapes):
 
 
 def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, reference,
-              cache=None, out=None, stats=None, stream=None):
+              cache=None, out=None, stats=None, stream=None, fallback=None):
     """One layer of Veda attention over q, k, v [S, H, D] (bf16 or float32).
 
     refs        : [(start, (T, H, W))] reference video spans (packed order)
@@ -235,27 +235,57 @@ def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, ref
     proj_q/k    : float32 [H, 3D, D] device tensors
     generated, reference : budget requests, e.g. ('sparsity', 0.9)
     cache       : optional dict holding plans between calls
+    stats       : optional dict; gets kept tile pairs ('entries') and the dense
+                  count ('dense'), see summary()
+    fallback    : optional callable(q, k, v) -> out, the caller's own attention.
+                  When libveda refuses the layout (VedaUnsupported: head_dim,
+                  alignment, sizes), it is called instead, with a warning: the
+                  node described on the comfyui-wiki Veda news pages (Spanish
+                  and French editions, section on requirements) reports the
+                  problem and lets the model keep its own attention for that
+                  run. Without a fallback the error is raised.
 
     References are tiled with their least-padding box unless the reference
     budget keeps everything, in which case their rows stay global (dense).
+    Every host-side check of every head group runs before the first launch.
     Returns out [S, H, D] in q's dtype.
     """
-    import torch
+    try:
+        return _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated,
+                          reference, cache, out, stats, stream)
+    except VedaUnsupported as e:
+        if fallback is None:
+            raise
+        import warnings
+        warnings.warn(f"veda attention does not support this layout ({e}); "
+                      "using the caller's attention", RuntimeWarning, stacklevel=2)
+        if stats is not None:
+            stats["fallback"] = str(e)
+        return fallback(q, k, v)
+
+
+def _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, reference,
+               cache, out, stats, stream):
     S, H, D = q.shape
     gen, ref = budget(generated), budget(reference)
     tile_refs = not _keeps_all(ref)
     cache = {} if cache is None else cache
+    groups = []
+    for shape, heads in _head_groups(head_shapes):
+        spans = [(s, g, None) for s, g in refs] if tile_refs else []
+        spans.append((target[0], target[1], shape))
+        info = veda_plan_query(spans, S)
+        sel = veda_select_query(info, gen, ref, D, len(heads))
+        groups.append((shape, heads, spans, sel))
+    import torch
     if out is None:
         out = torch.empty_like(q)
-    for shape, heads in _head_groups(head_shapes):
+    for shape, heads, spans, sel in groups:
         key = (tuple((int(s), tuple(g)) for s, g in refs), (int(target[0]), tuple(target[1])),
                shape, tile_refs, S, str(q.device))
         if key not in cache:
-            spans = [(s, g, None) for s, g in refs] if tile_refs else []
-            spans.append((target[0], target[1], shape))
             cache[key] = plan(spans, S, stream=stream, device=q.device)
         p = cache[key]
-        sel = veda_select_query(p.info, gen, ref, D, len(heads))
         idx = torch.tensor(heads, dtype=torch.long, device=q.device)
         pq = proj_q.index_select(0, idx).contiguous()
         pk = proj_k.index_select(0, idx).contiguous()
@@ -267,5 +297,16 @@ def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, ref
             stats.setdefault("entries", 0)
             stats["entries"] += len(heads) * sel.entries_per_head
             stats.setdefault("dense", 0.0)
-            stats["dense"] += len(heads) * (S / TILE) ** 2
+            stats["dense"] += len(heads) * float(p.info.n_tiles) ** 2
     return out
+
+
+def summary(stats) -> str:
+    """The per-run receipt of the node's status line (comfyui-wiki Veda news
+    pages, the node's output): the share of full attention computed, in tile
+    pairs, and the share skipped."""
+    if stats.get("fallback"):
+        return f"Attention computed by the caller's own attention ({stats['fallback']})"
+    dense = stats.get("dense", 0.0)
+    share = 100.0 * stats.get("entries", 0) / dense if dense else 0.0
+    return f"Attention computed: {share:.1f}% of full attention ({100.0 - share:.1f}% skipped)"

@@ -22,6 +22,7 @@ from oracle import attention, budget, layer, predictor, selection, tiles
 from gpu_common import GpuGroup, log, near_tie_rows, oracle_csr, to_device
 
 torch = pytest.importorskip("torch")
+import learned_block_sparse_amd as veda  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -229,3 +230,51 @@ def test_run_to_run_bitwise_determinism(name):
     assert torch.equal(outs[0], outs[1])
     for a, b in zip(*lists):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["ragged_refs", "padding"])
+def test_layer_attention_matches_oracle(name):
+    """The one-call layer (head groups by tile box, references tiled, cached
+    plans) against the oracle's whole layer, and its receipt."""
+    inp, dev, groups = _make(name)
+    wl = inp.workload
+    _, want = layer.run(inp)
+    pq, pk = dev["proj_q"], dev["proj_k"]
+    stats, cache = {}, {}
+    for _ in range(2):   # the second call reuses the cached plans
+        out = veda.attention(dev["q"], dev["k"], dev["v"], wl.refs, wl.target, wl.head_shapes,
+                             pq, pk, wl.generated, wl.reference, cache=cache, stats=stats)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - want)
+        tol_max, tol_mean = (F32_MAX, F32_MAX) if wl.dtype == "f32" else (BF16_MAX, BF16_MEAN)
+        assert err.max() <= tol_max and err.mean() <= tol_mean, (err.max(), err.mean())
+    kept = sum(int(np.count_nonzero(g.mask)) for g in groups)
+    assert stats["entries"] == 2 * kept
+    assert veda.summary(stats).startswith("Attention computed: ")
+
+
+@pytest.mark.parametrize("name", ["padding", "f32_padding"])
+def test_empty_tile_list_row_leaves_zeros(name):
+    """A CSR row with no tiles (veda_select never makes one; veda_attend takes
+    any CSR) writes zeros for its query rows and leaves every other row as
+    with the full lists. The last row (a global tile) is emptied, so the
+    other rows' offsets stay valid."""
+    inp, dev, groups = _make(name)
+    g = groups[0]
+    gg = GpuGroup(inp, dev, g.shape, g.heads)
+    out_a = gg.attend(dev)
+    ro = gg.row_offsets.clone()
+    ro[-1] = ro[-2]
+    out_b = veda.veda_attend(gg.info, gg.sel, gg.perm, gg.vc, dev["q"], dev["k"], dev["v"],
+                             gg.heads, ro, gg.cols)
+    torch.cuda.synchronize()
+    n = gg.info.n_tiles
+    perm = gg.perm.cpu().numpy()
+    last = perm[(n - 1) * 128:n * 128]
+    last = last[last >= 0]
+    a = out_a[:, gg.heads].float().cpu().numpy()
+    b = out_b[:, gg.heads].float().cpu().numpy()
+    assert (b[last] == 0).all()
+    keep = np.setdiff1d(np.arange(a.shape[0]), last)
+    assert np.array_equal(a[keep], b[keep])

@@ -183,3 +183,25 @@ def test_attend_refuses_unaddressable_bf16_rows(grid, seq_len, D, stride_s):
                          1, stride_s, D, stride_s, D, 1, heads, dummy, dummy, 0.0, None)
     assert st == 2
     assert "bf16 attend needs" in lib.veda_last_error().decode()
+
+
+def test_attention_unsupported_uses_callers_fallback():
+    """A head_dim libveda does not handle is refused on the host before any
+    launch; with a fallback the caller's own attention runs, with a warning,
+    and the receipt says so; without one the refusal is raised."""
+    import torch
+    q = torch.zeros(1024, 2, 96)
+    args = (q, q, q, [], (0, (4, 16, 16)), [None, None], None, None, ("sparsity", 0.9),
+            ("sparsity", 0.9))
+    with pytest.raises(veda.VedaUnsupported):
+        veda.attention(*args)
+    stats = {}
+    with pytest.warns(RuntimeWarning):
+        out = veda.attention(*args, stats=stats, fallback=lambda q, k, v: "callers-own")
+    assert out == "callers-own"
+    assert "caller's own attention" in veda.summary(stats)
+
+
+def test_summary_receipt():
+    assert veda.summary({"entries": 109, "dense": 1000.0}) == \
+        "Attention computed: 10.9% of full attention (89.1% skipped)"
