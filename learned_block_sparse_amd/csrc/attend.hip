@@ -332,8 +332,9 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
   //   A: softmax(t) first part (mask, max, rescale, probabilities of keys
   //      0..31), loads of K(t+1) spread through it
   //   B: softmax(t) rest (probabilities of keys 32..127, row sum)
-  //   C: P(t) V(t)
-  //   D: S(t+1) = K(t+1) Q^T, loads of V(t+1) spread through it
+  //   C: P(t) V(t), each MFMA's transposing V reads issued six MFMAs ahead
+  //   D: S(t+1) = K(t+1) Q^T, reads one k step ahead, loads of V(t+1) spread
+  //      through it
   // The two groups run two half-phases apart (the group on waves 0-3 behind),
   // so A and B of one group meet C and D of the other. K(t+1) has B and C
   // to land, V(t+1) has A and B. Every load is issued unconditionally (past
@@ -417,37 +418,38 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
     const Rows Rv = rows_of(list_at(t + 1));
     __builtin_amdgcn_s_setprio(1);   // MFMA half-phases issue first
     // ---- C
-    // P(t) V(t), the V^T fragments of each k step read one step ahead
+    // P(t) V(t) as 8 k steps x DB MFMAs. The transposing LDS reads have a
+    // long latency, so each MFMA's two reads are issued LA_PV MFMAs ahead
+    // (2 LA_PV reads in flight, within the 15 that lgkmcnt can count).
     {
-      s16x4 Vf[2][C::DB][2];
-      auto read_v = [&](int kstep, s16x4 (&dst)[C::DB][2]) {
+      constexpr int NM = 8 * C::DB;   // MFMAs of the P V half-phase
+      constexpr int LA_PV = 6;
+      s16x4 Vf[LA_PV + 1][2];
+      auto read_v1 = [&](int j, s16x4 (&dst)[2]) {
+        const int kstep = j / C::DB, db = j % C::DB;
         const int kb = kstep >> 1, e = kstep & 1;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const unsigned char *p0 = Vb + v_off[db] + (kb * 32 + e * 16) * C::ROW;
-          dst[db][0] = ds_read_tr(p0);
-          dst[db][1] = ds_read_tr(p0 + 8 * C::ROW);
-        }
+        const unsigned char *p0 = Vb + v_off[db] + (kb * 32 + e * 16) * C::ROW;
+        dst[0] = ds_read_tr(p0);
+        dst[1] = ds_read_tr(p0 + 8 * C::ROW);
       };
-      read_v(0, Vf[0]);
 #pragma unroll
-      for (int kstep = 0; kstep < 8; ++kstep) {
-        if (kstep + 1 < 8) read_v(kstep + 1, Vf[(kstep + 1) & 1]);
+      for (int j = 0; j < LA_PV; ++j) read_v1(j, Vf[j]);
+#pragma unroll
+      for (int j = 0; j < NM; ++j) {
+        if (j + LA_PV < NM) read_v1(j + LA_PV, Vf[(j + LA_PV) % (LA_PV + 1)]);
+        const int kstep = j / C::DB, db = j % C::DB;
         const int kb = kstep >> 1, e = kstep & 1;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const s16x4 lo = Vf[kstep & 1][db][0], hi4 = Vf[kstep & 1][db][1];
-          const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
-                                                                hi4[0], hi4[1], hi4[2], hi4[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8),
-                                                         pb[kb][e], o[db], 0, 0, 0);
-        }
+        const s16x4 lo = Vf[j % (LA_PV + 1)][0], hi4 = Vf[j % (LA_PV + 1)][1];
+        const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3],
+                                                              hi4[0], hi4[1], hi4[2], hi4[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8),
+                                                       pb[kb][e], o[db], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA_PV, 0);
 #pragma unroll
-      for (int kstep = 0; kstep < 8; ++kstep) {
-        if (kstep + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, C::DB, 0);
+      for (int j = 0; j < NM; ++j) {
+        if (j + LA_PV < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     }
     barrier_vm<NL>();   // K(t+1) landed; every wave is done with V(t)
