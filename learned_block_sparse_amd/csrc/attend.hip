@@ -307,31 +307,37 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
   auto exps8 = [&](int kb, int h) {
 #pragma unroll
     for (int i = 8 * h; i < 8 * h + 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_run));
+      const float x = fmaf(s[kb][i], a.scale_log2, -m_run);
+      s[kb][i] = x;   // kept for a recompute against a raised m_run
+      const float p = __builtin_amdgcn_exp2f(x);
       pb[kb][h][i % 8] = static_cast<__bf16>(p);
       racc[i & 3] += p;
     }
   };
-  // Lazy rescale: takes the running max to mx (log2 units) only when mx
-  // exceeds it by more than 8, so probabilities stay <= 256 (exact range in
-  // fp32 and bf16), and scales O and the row sum to match.
-  auto rescale = [&](float mx) {
-    if (mx > m_run + 8.0f) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
-      m_run = mx;
-      l_run *= alpha;
+  // The row's reference value m_run (log2 units) is any value the
+  // probabilities exp2(scale s - m_run) stay finite against: softmax is the
+  // same for every choice, and bf16 and fp32 keep their relative precision at
+  // any magnitude. It is set to the first tile's row max and raised only when
+  // a tile's probabilities sum past 2^20 (or overflow); that tile is then
+  // recomputed against the exact running max, with O and the row sum scaled
+  // to match. Every tile's sum stays <= 2^20, so O and the row sum stay far
+  // inside fp32 range.
+  auto s_max = [&]() {
+    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
+      for (int i = 0; i < 16; ++i) mx4[i & 3] = fmaxf(mx4[i & 3], s[kb][i]);
+    return pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
   };
+  auto tile_sum = [&]() { return pair_sum((racc[0] + racc[1]) + (racc[2] + racc[3])); };
 
   // Schedule. Each group's work per kept tile t is cut into four
   // half-phases, each closed by a workgroup barrier:
-  //   A: softmax(t) first part (mask, max, rescale, probabilities of keys
-  //      0..31), loads of K(t+1) spread through it
-  //   B: softmax(t) rest (probabilities of keys 32..127, row sum)
+  //   A: softmax(t) first part (mask, probabilities of keys 0..31), loads
+  //      of K(t+1) spread through it
+  //   B: softmax(t) rest (probabilities of keys 32..127, row sum, the rare
+  //      recompute against a raised reference value)
   //   C: P(t) V(t), each MFMA's transposing V reads issued six MFMAs ahead
   //   D: S(t+1) = K(t+1) Q^T, reads one k step ahead, loads of V(t+1) spread
   //      through it
@@ -372,9 +378,13 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
     barrier_lds();
   }
   int32_t vc_cur = vcount[list_at(0)];
+  int32_t j1 = list_at(1);   // tile t+1
 
   for (int t = 0; t < n_t; ++t) {
-    const int32_t vc_next = vcount[list_at(t + 1)];
+    // Scalar loads for the next tiles, issued here a half-phase or more
+    // before their first use (the barrier closing A waits for them).
+    const int32_t j2 = list_at(t + 2);
+    const int32_t vc_next = vcount[j1];
     __builtin_amdgcn_s_setprio(0);   // vector half-phases yield to the other group's MFMAs
     // ---- A
     if (vc_cur < VEDA_TILE) {
@@ -388,12 +398,7 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + 8 * (i / 4) + (i % 4) >= thr) s[kb][i] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    rescale(pair_max(mx) * a.scale_log2);
+    if (t == 0) m_run = s_max() * a.scale_log2;   // O and the row sum are still zero
     racc[0] = racc[1] = racc[2] = racc[3] = 0.0f;
     // K(t+1) streams in between chunks of probabilities, a few loads at a
     // time, so no wave waits on the address unit's queue.
@@ -413,9 +418,39 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
     exps8(2, 1);
     exps8(3, 0);
     exps8(3, 1);
-    l_run += pair_sum((racc[0] + racc[1]) + (racc[2] + racc[3]));
+    // the packed probabilities exist here (not sunk past the branch below,
+    // which would keep their fp32 sources live across it)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pb[kb][h]));
+    float ts = tile_sum();
+    if (__builtin_amdgcn_ballot_w64(!(ts <= 0x1p20f)) != 0) {   // rare; also catches inf and NaN
+      // s now holds scale s - m_run: raise m_run by the excess d
+      const float d = fmaxf(0.0f, s_max());
+      if (d > 0.0f) {
+        const float alpha = __builtin_amdgcn_exp2f(-d);
+        m_run += d;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+      racc[0] = racc[1] = racc[2] = racc[3] = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(s[kb][i] - d);
+          pb[kb][i / 8][i % 8] = static_cast<__bf16>(p);
+          racc[i & 3] += p;
+        }
+      ts = tile_sum();
+    }
+    l_run += ts;
     barrier_vm<NL>();   // V(t) landed in every wave (K(t+1) may not)
-    const Rows Rv = rows_of(list_at(t + 1));
+    const Rows Rv = rows_of(j1);
     __builtin_amdgcn_s_setprio(1);   // MFMA half-phases issue first
     // ---- C
     // P(t) V(t) as 8 k steps x DB MFMAs. The transposing LDS reads have a
@@ -454,12 +489,13 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
     }
     barrier_vm<NL>();   // K(t+1) landed; every wave is done with V(t)
     // ---- D
-    Rk = rows_of(list_at(t + 2));
+    Rk = rows_of(j2);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     scores_with_v(Rv);
     barrier_lds();     // every wave is done with K(t+1)
     vc_cur = vc_next;
+    j1 = j2;
   }
   if constexpr (GROUP == 0) {
     barrier_lds();

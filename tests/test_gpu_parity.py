@@ -278,3 +278,63 @@ def test_empty_tile_list_row_leaves_zeros(name):
     assert (b[last] == 0).all()
     keep = np.setdiff1d(np.arange(a.shape[0]), last)
     assert np.array_equal(a[keep], b[keep])
+
+
+def _scaled_keys(kind):
+    """padding workload with some key rows scaled by a power of two (exact in
+    bf16), so a later tile's scores jump far past the first tile's row max
+    ('late'), one key's scores overflow exp2 outright ('one_key'), or the
+    first tiles carry the largest scores ('early')."""
+    inp = workloads.generate("padding")
+    k = inp.k.copy()
+    S = k.shape[0]
+    if kind == "late":
+        k[S // 2:] *= 8.0
+    elif kind == "one_key":
+        k[S - 200] *= 64.0
+    else:
+        k[: S // 8] *= 4.0
+    return dataclasses.replace(inp, k=k)
+
+
+@pytest.mark.parametrize("kind", ["late", "one_key", "early"])
+def test_large_score_jumps(kind):
+    """The bf16 kernel keeps a per-row reference value from the first tile and
+    recomputes a tile against a raised one only when the tile's probabilities
+    sum past 2^20 or overflow. Inputs where that happens must still match the
+    exact softmax of the oracle."""
+    inp = _scaled_keys(kind)
+    D = inp.q.shape[2]
+    c = np.log2(np.e) / np.sqrt(D)
+    if kind != "early":
+        # the recompute really is exercised: for some query rows a scaled key
+        # scores more than 20 (log2 units) above every key of tile 0
+        q0 = inp.q[:256, 0].astype(np.float64)
+        first = (q0 @ inp.k[:128, 0].astype(np.float64).T).max(axis=1) * c
+        lo = inp.q.shape[0] // 2 if kind == "late" else inp.q.shape[0] - 200
+        hi = inp.q.shape[0] if kind == "late" else lo + 1
+        jump = (q0 @ inp.k[lo:hi, 0].astype(np.float64).T).max(axis=1) * c - first
+        assert (jump > 20).sum() >= 8, jump.max()
+    dev = to_device(inp)
+    groups, _ = layer.run(inp, do_attend=False)
+    out = torch.full_like(dev["q"], float("nan"))
+    for g in groups:
+        GpuGroup(inp, dev, g.shape, g.heads, scores_mode=2, oracle_scores=g.scores).attend(dev, out=out)
+    torch.cuda.synchronize()
+    out_np = out.float().cpu().numpy()
+    assert np.isfinite(out_np).all()
+    # Peaked rows put the output near one value row, up to max|v| in size, so
+    # the bf16 roundings that are harmless for the workloads' smooth rows show
+    # here: the output's own rounding (half an ulp, <= 2^-8 |o|) and the
+    # probabilities' (each <= 2^-9 relative, so <= 2^-9 max|v| on a weighted
+    # mean, doubled for margin). A wrong rescale would be off by O(|v|).
+    vmax = float(np.abs(inp.v).max())
+    for g in groups:
+        want = attention.attend(inp.q, inp.k, inp.v, g.layout, g.mask, g.heads)
+        got = out_np[:, g.heads, :].astype(np.float64)
+        err = np.abs(got - want)
+        bound = 2.0 ** -8 * (np.abs(want) + vmax)
+        log(f"[attend] jumps_{kind} max={err.max():.3e} mean={err.mean():.3e} "
+            f"worst/bound={(err / bound).max():.2f}")
+        assert (err <= bound).all()
+        assert err.mean() <= 2e-3
