@@ -338,7 +338,7 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
   //      of K(t+1) spread through it
   //   B: softmax(t) rest (probabilities of keys 32..127, row sum, the rare
   //      recompute against a raised reference value)
-  //   C: P(t) V(t), each MFMA's transposing V reads issued six MFMAs ahead
+  //   C: P(t) V(t), each MFMA's transposing V reads issued four MFMAs ahead
   //   D: S(t+1) = K(t+1) Q^T, reads one k step ahead, loads of V(t+1) spread
   //      through it
   // The two groups run two half-phases apart (the group on waves 0-3 behind),
@@ -458,7 +458,7 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
     // (2 LA_PV reads in flight, within the 15 that lgkmcnt can count).
     {
       constexpr int NM = 8 * C::DB;   // MFMAs of the P V half-phase
-      constexpr int LA_PV = 6;
+      constexpr int LA_PV = 4;
       s16x4 Vf[LA_PV + 1][2];
       auto read_v1 = [&](int j, s16x4 (&dst)[2]) {
         const int kstep = j / C::DB, db = j % C::DB;
