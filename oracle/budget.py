@@ -53,17 +53,29 @@ def per_row(budget, real_tokens, n_cols):
 
 
 def split(b, n_cols):
-    """(k_lo, k_hi, frac) with 1 <= k_lo <= k_hi <= n_cols.
+    """(k_lo, k_hi, frac) for a per-row budget b over a block of n_cols key
+    tiles (veda_core.py § budgets, _split), with 1 <= k_lo <= k_hi <= n_cols.
 
-    A budget of at least n_cols keeps everything: (n, n, 0). Otherwise
-    k_lo = clamp(floor(b), 1, n), k_hi = min(k_lo + 1, n), and frac is
-    b - k_lo clipped to [0, 1] and rounded to 12 decimals (Python's
-    correctly rounded decimal round).
+    A budget of n_cols or more keeps the whole block, (n, n, 0). Otherwise a
+    row keeps the whole part of b, at least one tile and at most n_cols, and
+    one tile more on the rows the Bresenham pattern picks; that pattern runs
+    on the leftover b - k_lo, clipped to [0, 1] and rounded to 12 decimal
+    places with Python's correctly rounded round().
     """
     if b >= n_cols:
         return n_cols, n_cols, 0.0
-    lo = min(max(1, math.floor(b)), n_cols)
-    return lo, min(lo + 1, n_cols), round(min(max(b - lo, 0.0), 1.0), 12)
+    k_lo = int(math.floor(b))
+    if k_lo < 1:
+        k_lo = 1
+    if k_lo > n_cols:
+        k_lo = n_cols
+    k_hi = k_lo + 1 if k_lo < n_cols else n_cols
+    leftover = b - k_lo
+    if leftover < 0.0:
+        leftover = 0.0
+    if leftover > 1.0:
+        leftover = 1.0
+    return k_lo, k_hi, round(leftover, 12)
 
 
 def bresenham(n_rows, frac):

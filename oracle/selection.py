@@ -12,13 +12,17 @@ from .budget import keeps_all, per_row, split, bresenham
 
 
 def column_blocks(layout, generated, reference):
-    """[(start, stop, budget, real_tokens)]: the reference tiles (when there
-    are any) and the target tiles each get their own top-k
-    (veda_core.py § selection, column_blocks)."""
-    target = (layout.n_ref, layout.n_video, generated, layout.target_tokens)
-    if layout.n_ref == 0:
-        return [target]
-    return [(0, layout.n_ref, reference, layout.ref_tokens), target]
+    """[(start, stop, budget, real_tokens)] (veda_core.py § selection,
+    column_blocks): the key tiles split into independent top-k blocks. The
+    target tiles always form one block under the generated budget; when the
+    layout holds reference tiles they form a block of their own, first, under
+    the reference budget, so that the target's neighbours cannot crowd the
+    references out of a single shared top-k."""
+    blocks = []
+    if layout.n_ref > 0:
+        blocks.append((0, layout.n_ref, reference, layout.ref_tokens))
+    blocks.append((layout.n_ref, layout.n_video, generated, layout.target_tokens))
+    return blocks
 
 
 def block_params(layout, blocks):

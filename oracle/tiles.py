@@ -123,48 +123,59 @@ class Layout:
         return ids[ids >= 0]
 
 
+def _check_spans(spans, seq_len):
+    """Refuses span lists the packing cannot use (veda_core.py § tiles,
+    build_layout): there must be a target span; spans come in packed order,
+    each one beginning no earlier than where the previous one ended and lying
+    inside [0, seq_len). Reading: a negative start is refused as well (the
+    page tests only order, overlap and overrun)."""
+    if len(spans) == 0:
+        raise VedaError("no video span given: the generated video must be tiled")
+    prev_end = 0
+    for start, grid, _ in spans:
+        end = start + grid[0] * grid[1] * grid[2]
+        if start < 0 or start < prev_end or end > seq_len:
+            raise VedaError(f"video span [{start}, {end}) is out of packed order or "
+                            f"outside the sequence of {seq_len} rows")
+        prev_end = end
+
+
 def build_layout(spans, seq_len):
     """One permutation of the packed sequence.
 
     veda_core.py § tiles, build_layout: `spans` = [(start, grid, shape)] in
-    packed order with the target last. A span that starts before the end of
-    the previous one, or runs past seq_len, is refused; so is an empty span
-    list. Video tiles come first, in span order. Every row no span covers is
-    a global row: those go after the video tiles in ascending order, 128 per
-    tile, the last tile padded with -1.
-
-    Reading: a negative start is refused too (the pages only test overlap
-    and overrun).
+    packed order with the target last. The tiles of each span come first, in
+    span order (span_tiles). Every row that no span covers is a global row
+    (text, audio, conditions kept whole); the global rows follow the video
+    tiles in ascending row order, 128 to a tile, and the last global tile is
+    padded with -1.
     """
-    if not spans:
-        raise VedaError("the target span must be tiled")
-    covered = np.zeros(seq_len, dtype=bool)
-    tiles = []
-    stop = 0
-    for start, grid, shape in spans:
-        rows = grid[0] * grid[1] * grid[2]
-        if start < stop or start < 0 or start + rows > seq_len:
-            raise VedaError(f"span at {start} overlaps another or runs past {seq_len}")
-        stop = start + rows
-        covered[start:stop] = True
-        tiles.append(span_tiles(start, grid, shape))
-    video = np.concatenate(tiles, axis=0)
-    rest = np.nonzero(~covered)[0]
-    n_global = _ceil_div(len(rest), TILE)
-    tail = np.full(n_global * TILE, -1, dtype=np.int64)
-    tail[:len(rest)] = rest
-    perm = np.concatenate([video.reshape(-1), tail])
-    n_tiles = video.shape[0] + n_global
-    count = np.zeros(n_tiles, dtype=np.int64)
+    _check_spans(spans, seq_len)
+    video = [span_tiles(start, grid, shape) for start, grid, shape in spans]
+    n_video = sum(t.shape[0] for t in video)
+
+    in_span = [False] * seq_len
+    for start, grid, _ in spans:
+        for r in range(start, start + grid[0] * grid[1] * grid[2]):
+            in_span[r] = True
+    global_rows = [r for r in range(seq_len) if not in_span[r]]
+    n_global = _ceil_div(len(global_rows), TILE)
+    global_slots = global_rows + [-1] * (n_global * TILE - len(global_rows))
+
+    perm = np.array([r for t in video for r in t.reshape(-1)] + global_slots, dtype=np.int64)
+    n_tiles = n_video + n_global
+    valid = np.zeros(n_tiles, dtype=np.int64)
     for a in range(n_tiles):
-        count[a] = int(np.sum(perm[a * TILE:(a + 1) * TILE] >= 0))
+        for slot in range(a * TILE, (a + 1) * TILE):
+            if perm[slot] >= 0:
+                valid[a] += 1
+
+    def rows_of(sp):
+        return sum(g[0] * g[1] * g[2] for _, g, _ in sp)
+
     return Layout(
-        perm=perm, valid_count=count,
-        n_video=video.shape[0],
-        n_ref=sum(t.shape[0] for t in tiles[:-1]),
-        n_global=n_global, n_tiles=n_tiles,
-        ref_tokens=sum(g[0] * g[1] * g[2] for _, g, _ in spans[:-1]),
-        target_tokens=spans[-1][1][0] * spans[-1][1][1] * spans[-1][1][2],
-        seq_len=seq_len,
-        shapes=[s for _, _, s in spans],
+        perm=perm, valid_count=valid, n_video=n_video,
+        n_ref=n_video - video[-1].shape[0], n_global=n_global, n_tiles=n_tiles,
+        ref_tokens=rows_of(spans[:-1]), target_tokens=rows_of(spans[-1:]),
+        seq_len=seq_len, shapes=[s for _, _, s in spans],
     )

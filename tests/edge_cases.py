@@ -1,0 +1,41 @@
+"""Small hand-made layer geometries that the five benchmark workloads do not
+cover (inputs only, no method arithmetic): shared by the oracle pins and the
+GPU parity tests."""
+import dataclasses
+
+import workloads
+
+_base = workloads.get("padding")
+
+EDGE = {
+    # one video cell (a tile with a single real row) between text rows
+    "one_cell": dataclasses.replace(
+        _base, name="one_cell", index=11, seq_len=10, n_heads=2,
+        target=(3, (1, 1, 1)), head_shapes=(None, None), generated=("ratio", 0.5),
+        reference=("ratio", 0.5)),
+    # two reference spans and a ragged target, globals before, between and after
+    "ragged_refs": dataclasses.replace(
+        _base, name="ragged_refs", index=12, seq_len=700, n_heads=3,
+        head_dim=128, refs=((5, (1, 5, 6)), (40, (2, 3, 4))), target=(90, (3, 5, 37)),
+        head_shapes=(None, (1, 8, 16), None), generated=("sparsity", 0.5),
+        reference=("sparsity", 0.6)),
+    # keep-all budget: must equal dense attention
+    "keep_all": dataclasses.replace(_base, name="keep_all", index=13,
+                                    generated=("ratio", 1.0), reference=("ratio", 1.0)),
+    # a tile budget larger than the block
+    "tiles_big": dataclasses.replace(_base, name="tiles_big", index=14,
+                                     generated=("tiles", 100.0), reference=("tiles", 100.0)),
+    # fp32 with global rows and padding
+    "f32_padding": dataclasses.replace(_base, name="f32_padding", index=15,
+                                       dtype="f32", head_dim=128),
+    # a reference span whose budget keeps everything: it is not tiled, its
+    # rows join the text rows as global rows
+    "refs_whole": dataclasses.replace(
+        _base, name="refs_whole", index=16, seq_len=1500, n_heads=4,
+        refs=((0, (2, 5, 12)),), target=(130, (5, 12, 20)), head_shapes=(None,) * 4,
+        generated=("ratio", 0.25), reference=("ratio", 1.0)),
+}
+
+
+def get(name):
+    return EDGE.get(name) or workloads.get(name)
