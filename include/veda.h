@@ -169,9 +169,11 @@ veda_status veda_select_query(const veda_plan_info *info, veda_budget generated,
  *   scores        device double[n_heads][n_video][n_video] or NULL.
  *   scores_mode   0: compute logits into the workspace; 1: compute them and
  *                 also write them to `scores`; 2: skip pooling and scoring
- *                 and select from the given `scores`.
- *   workspace     device scratch of at least sel->workspace_bytes (mode 2
- *                 needs none).
+ *                 and select from the given `scores`. In mode 0, when every
+ *                 column block keeps all its tiles (ratio budgets >= 1), no
+ *                 logit is needed and pooling and scoring are skipped.
+ *   workspace     device scratch of at least sel->workspace_bytes (mode 2,
+ *                 and mode 0 with every block keeping all, need none).
  * Selection is exact given the logits: rank by logit descending, lower
  * column first on ties; own tile +inf; logits and pooling are fp64.
  * Asynchronous on `stream`. */
@@ -209,6 +211,20 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
                         int64_t out_stride_s, int64_t out_stride_h, int32_t n_heads_total,
                         const int32_t *heads, const int32_t *row_offsets, const int32_t *cols,
                         float scale, hipStream_t stream);
+
+/* Host only, synchronous: every check veda_attend makes (the arguments, the
+ * head list, alignment and the bf16 path's addressing limits), with the same
+ * arguments but no scale and no stream, and nothing launched. A layer made of
+ * several calls can refuse a layout before it launches anything for it.
+ * Pointers are tested for NULL and alignment only, never dereferenced.
+ * Returns what veda_attend would return before launching. */
+veda_status veda_attend_check(const veda_plan_info *info, const veda_select_info *sel,
+                              const int32_t *perm, const int32_t *valid_count,
+                              const void *q, const void *k, const void *v, const void *out,
+                              veda_dtype dtype, int64_t stride_s, int64_t stride_h,
+                              int64_t out_stride_s, int64_t out_stride_h, int32_t n_heads_total,
+                              const int32_t *heads, const int32_t *row_offsets,
+                              const int32_t *cols);
 
 #ifdef __cplusplus
 }

@@ -16,9 +16,10 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import Budget, PlanInfo, SelectInfo, Span, TILE
 
-__all__ = ["VedaError", "VedaUnsupported", "VedaDeviceError", "budget", "summary", "veda_plan_query",
-           "veda_plan", "veda_select_query", "veda_select", "veda_attend", "Plan", "plan",
-           "attention", "version", "library_path"]
+__all__ = ["VedaError", "VedaUnsupported", "VedaDeviceError", "budget", "summary", "receipt",
+           "veda_plan_query", "veda_plan", "veda_select_query", "veda_select", "veda_attend",
+           "veda_attend_check", "Plan", "plan", "Policy", "parse_index_list", "attention",
+           "version", "library_path"]
 
 
 class VedaError(ValueError):
@@ -164,10 +165,11 @@ def veda_select(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, heads,
             if p is None or p.dtype != torch.float32 or not p.is_contiguous() or \
                     tuple(p.shape) != (nh, 3 * sel.head_dim, sel.head_dim):
                 raise VedaError("proj_q / proj_k must be contiguous float32 [n_heads, 3D, D]")
-        if workspace is None:
+        selects = any(not sel.blocks[b].keep_all for b in range(sel.n_blocks))
+        if workspace is None and (scores_mode == 1 or selects):
             workspace = torch.empty(sel.workspace_bytes, dtype=torch.uint8, device=dev)
         dt, ss, sh, ht = _dtype_code(q), q.stride(0), q.stride(1), q.shape[1]
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     else:
         dt, ss, sh, ht, ws_bytes = _lib.BF16, 0, 0, max(int(h) for h in heads) + 1, 0
     if scores is not None and (scores.dtype != torch.float64 or not scores.is_contiguous()):
@@ -201,6 +203,20 @@ def veda_attend(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, v, hea
     return out
 
 
+def veda_attend_check(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, v, heads,
+                      row_offsets, cols, out):
+    """Every check veda_attend makes, on the host, launching nothing; raises
+    like veda_attend would."""
+    _check_qkv(q, k, v)
+    harr, nh = _heads_array(heads)
+    if nh != sel.n_heads:
+        raise VedaError("len(heads) differs from the n_heads given to veda_select_query")
+    _check(_lib.load().veda_attend_check(
+        C.byref(info), C.byref(sel), _ptr(perm), _ptr(valid_count), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(out), _dtype_code(q), q.stride(0), q.stride(1), out.stride(0), out.stride(1),
+        q.shape[1], harr, _ptr(row_offsets), _ptr(cols)))
+
+
 # ------------------------------------------------------------- one layer --
 @dataclass
 class Plan:
@@ -225,8 +241,55 @@ def _head_groups(head_shapes):
     return list(groups.items())
 
 
+def parse_index_list(text) -> frozenset:
+    """'0, 1, 47-49' -> {0, 1, 47, 48, 49}: the node's format for its
+    full_attention_layers / full_attention_steps inputs (0-based DiT blocks and
+    sampling steps; comfyui-wiki Veda news pages, French and Korean editions,
+    the node's input table). Empty or None gives the empty set."""
+    if text is None:
+        return frozenset()
+    if not isinstance(text, str):
+        return frozenset(int(x) for x in text)
+    out = set()
+    for part in text.replace(";", ",").split(","):
+        part = part.strip()
+        if not part:
+            continue
+        lo, sep, hi = part.partition("-")
+        try:
+            a = int(lo)
+            b = int(hi) if sep else a
+        except ValueError:
+            raise VedaError(f"not an index or a range: {part!r}") from None
+        if a < 0 or b < a:
+            raise VedaError(f"bad range {part!r}: indices are 0-based and ranges ascend")
+        out.update(range(a, b + 1))
+    return frozenset(out)
+
+
+@dataclass(frozen=True)
+class Policy:
+    """Which calls keep full attention: listed DiT blocks (layers) and
+    sampling steps, as the node's full_attention_layers and
+    full_attention_steps inputs set them."""
+    full_attention_layers: frozenset = frozenset()
+    full_attention_steps: frozenset = frozenset()
+
+    @classmethod
+    def from_text(cls, layers="", steps=""):
+        return cls(parse_index_list(layers), parse_index_list(steps))
+
+    def keeps_full(self, layer=None, step=None) -> bool:
+        return (layer is not None and layer in self.full_attention_layers) or \
+            (step is not None and step in self.full_attention_steps)
+
+
+_KEEP_ALL = ("ratio", 1.0)
+
+
 def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, reference,
-              cache=None, out=None, stats=None, stream=None, fallback=None):
+              cache=None, out=None, stats=None, stream=None, fallback=None, layer=None,
+              step=None, policy=None):
     """One layer of Veda attention over q, k, v [S, H, D] (bf16 or float32).
 
     refs        : [(start, (T, H, W))] reference video spans (packed order)
@@ -235,8 +298,10 @@ def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, ref
     proj_q/k    : float32 [H, 3D, D] device tensors
     generated, reference : budget requests, e.g. ('sparsity', 0.9)
     cache       : optional dict holding plans between calls
-    stats       : optional dict; gets kept tile pairs ('entries') and the dense
-                  count ('dense'), see summary()
+    out         : optional [S, H, D] output (q's dtype); allocated if None
+    stats       : optional dict accumulating the run's receipt (see receipt()):
+                  'entries' tile pairs computed, 'dense' the full-attention
+                  count (S/128)^2 per head, 'sparse_calls', 'dense_calls'
     fallback    : optional callable(q, k, v) -> out, the caller's own attention.
                   When libveda refuses the layout (VedaUnsupported: head_dim,
                   alignment, sizes), it is called instead, with a warning: the
@@ -244,15 +309,27 @@ def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, ref
                   and French editions, section on requirements) reports the
                   problem and lets the model keep its own attention for that
                   run. Without a fallback the error is raised.
+    layer, step, policy : with a Policy that lists this layer or step, the
+                  call keeps full attention: the caller's `fallback` when one
+                  is given (the model's own attention), else libveda's
+                  kernels with every tile kept, which is exact dense
+                  attention. It counts as a dense call in the receipt.
 
     References are tiled with their least-padding box unless the reference
     budget keeps everything, in which case their rows stay global (dense).
-    Every host-side check of every head group runs before the first launch.
+    Every host-side check of every head group, the attend limits included,
+    runs before the first launch, so a refusal leaves the device untouched.
     Returns out [S, H, D] in q's dtype.
     """
+    dense = policy is not None and policy.keeps_full(layer, step)
+    if dense:
+        generated = reference = _KEEP_ALL
     try:
-        return _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated,
-                          reference, cache, out, stats, stream)
+        if dense and fallback is not None:
+            res = _into(out, fallback(q, k, v))
+        else:
+            res = _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated,
+                             reference, cache, out, None if dense else stats, stream)
     except VedaUnsupported as e:
         if fallback is None:
             raise
@@ -261,43 +338,69 @@ def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, ref
                       "using the caller's attention", RuntimeWarning, stacklevel=2)
         if stats is not None:
             stats["fallback"] = str(e)
-        return fallback(q, k, v)
+        return _into(out, fallback(q, k, v))
+    if stats is not None:
+        key = "dense_calls" if dense else "sparse_calls"
+        stats[key] = stats.get(key, 0) + 1
+        if dense:
+            full = q.shape[1] * (q.shape[0] / TILE) ** 2
+            stats["entries"] = stats.get("entries", 0) + full
+            stats["dense"] = stats.get("dense", 0.0) + full
+    return res
+
+
+def _into(out, res):
+    """The caller's own attention result, written into `out` when one was given."""
+    if out is None:
+        return res
+    out.copy_(res)
+    return out
 
 
 def _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, reference,
                cache, out, stats, stream):
+    import torch
     S, H, D = q.shape
     gen, ref = budget(generated), budget(reference)
     tile_refs = not _keeps_all(ref)
     cache = {} if cache is None else cache
+    if out is None:
+        out = torch.empty_like(q)
+    # host side of every group first: layouts, budgets, buffers, attend limits
     groups = []
     for shape, heads in _head_groups(head_shapes):
         spans = [(s, g, None) for s, g in refs] if tile_refs else []
         spans.append((target[0], target[1], shape))
-        info = veda_plan_query(spans, S)
-        sel = veda_select_query(info, gen, ref, D, len(heads))
-        groups.append((shape, heads, spans, sel))
-    import torch
-    if out is None:
-        out = torch.empty_like(q)
-    for shape, heads, spans, sel in groups:
         key = (tuple((int(s), tuple(g)) for s, g in refs), (int(target[0]), tuple(target[1])),
                shape, tile_refs, S, str(q.device))
-        if key not in cache:
-            cache[key] = plan(spans, S, stream=stream, device=q.device)
-        p = cache[key]
+        p = cache.get(key)
+        if p is None:
+            info = veda_plan_query(spans, S)
+            p = Plan(info, torch.empty(info.n_slots, dtype=torch.int32, device=q.device),
+                     torch.empty(info.n_tiles, dtype=torch.int32, device=q.device))
+            p.built = False
+        sel = veda_select_query(p.info, gen, ref, D, len(heads))
+        ro = torch.empty(p.info.n_tiles + 1, dtype=torch.int32, device=q.device)
+        cols = torch.empty(len(heads) * sel.entries_per_head, dtype=torch.int32, device=q.device)
+        veda_attend_check(p.info, sel, p.perm, p.valid_count, q, k, v, heads, ro, cols, out)
+        groups.append((key, p, heads, sel, ro, cols))
+    for key, p, heads, sel, ro, cols in groups:
+        if not getattr(p, "built", True):
+            veda_plan(p.info, p.perm, p.valid_count, stream=stream)
+            p.built = True
+            cache[key] = p
         idx = torch.tensor(heads, dtype=torch.long, device=q.device)
         pq = proj_q.index_select(0, idx).contiguous()
         pk = proj_k.index_select(0, idx).contiguous()
-        ro, cols = veda_select(p.info, sel, p.perm, p.valid_count, q, k, heads, pq, pk,
-                               stream=stream)
+        veda_select(p.info, sel, p.perm, p.valid_count, q, k, heads, pq, pk, row_offsets=ro,
+                    cols=cols, stream=stream)
         veda_attend(p.info, sel, p.perm, p.valid_count, q, k, v, heads, ro, cols, out=out,
                     stream=stream)
         if stats is not None:
-            stats.setdefault("entries", 0)
-            stats["entries"] += len(heads) * sel.entries_per_head
-            stats.setdefault("dense", 0.0)
-            stats["dense"] += len(heads) * float(p.info.n_tiles) ** 2
+            stats["entries"] = stats.get("entries", 0) + len(heads) * sel.entries_per_head
+            # full attention: (S / 128)^2 tile pairs per head (page `veda_core.py`,
+            # section "one layer", the run's stats), whatever the padding
+            stats["dense"] = stats.get("dense", 0.0) + len(heads) * (S / TILE) ** 2
     return out
 
 
@@ -310,3 +413,14 @@ def summary(stats) -> str:
     dense = stats.get("dense", 0.0)
     share = 100.0 * stats.get("entries", 0) / dense if dense else 0.0
     return f"Attention computed: {share:.1f}% of full attention ({100.0 - share:.1f}% skipped)"
+
+
+def receipt(stats, kernel="HIP bf16 MFMA (gfx950)") -> str:
+    """The run's receipt: the kernel that ran, the share line of summary(),
+    and the count of sparse and dense (full-attention) calls, as the Vflash
+    guide's Veda receipts report them."""
+    lines = [f"Veda done \u00b7 {kernel}", summary(stats)]
+    sp, dn = stats.get("sparse_calls", 0), stats.get("dense_calls", 0)
+    if sp or dn:
+        lines.append(f"Calls: {sp} sparse, {dn} dense")
+    return "\n".join(lines)

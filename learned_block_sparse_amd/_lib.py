@@ -9,7 +9,9 @@ import ctypes as C
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libveda.so")
+# VEDA_LIBRARY names another build of the library to load (the tests use it
+# for the sanitizer build of the host-only entry points).
+LIB_PATH = os.environ.get("VEDA_LIBRARY") or os.path.join(PKG, "libveda.so")
 
 TILE = 128
 MAX_SPANS = 16
@@ -20,7 +22,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_DEVICE = 0, 1, 2, 3
 F32, BF16 = 0, 1
 
 EXPORTS = ("veda_last_error", "veda_version", "veda_plan_query", "veda_plan",
-           "veda_select_query", "veda_select", "veda_attend")
+           "veda_select_query", "veda_select", "veda_attend", "veda_attend_check")
 
 
 class Span(C.Structure):
@@ -54,6 +56,27 @@ class SelectInfo(C.Structure):
 _lib = None
 
 
+class _HostOnly:
+    """A host-only build: prototypes of launching entry points are accepted
+    and dropped; calling one raises."""
+
+    def __init__(self, lib):
+        object.__setattr__(self, "_l", lib)
+
+    def __getattr__(self, name):
+        if hasattr(self._l, name):
+            return getattr(self._l, name)
+        raise AttributeError(f"{name} is not in this host-only build of libveda")
+
+    def __setattr__(self, name, value):
+        setattr(self._l, name, value)
+
+
+def has_kernels() -> bool:
+    """Whether the loaded library holds the kernels and launching entry points."""
+    return not isinstance(load(), _HostOnly)
+
+
 def load():
     """The loaded libveda (built in-tree); raises if it is missing."""
     global _lib
@@ -65,22 +88,27 @@ def load():
             "`python -m learned_block_sparse_amd.build` (there is no fallback path)")
     lib = C.CDLL(LIB_PATH)
     P, I32, I64, D, F, SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_double, C.c_float, C.c_size_t
-    lib.veda_last_error.restype = C.c_char_p
-    lib.veda_last_error.argtypes = []
-    lib.veda_version.restype = C.c_char_p
-    lib.veda_version.argtypes = []
-    lib.veda_plan_query.restype = C.c_int
-    lib.veda_plan_query.argtypes = [C.POINTER(Span), I32, I64, C.POINTER(PlanInfo)]
-    lib.veda_plan.restype = C.c_int
-    lib.veda_plan.argtypes = [C.POINTER(PlanInfo), P, P, P]
-    lib.veda_select_query.restype = C.c_int
-    lib.veda_select_query.argtypes = [C.POINTER(PlanInfo), Budget, Budget, I32, I32,
-                                      C.POINTER(SelectInfo)]
-    lib.veda_select.restype = C.c_int
-    lib.veda_select.argtypes = [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P, C.c_int,
-                                I64, I64, I32, C.POINTER(I32), P, P, P, P, P, I32, P, SZ, P]
-    lib.veda_attend.restype = C.c_int
-    lib.veda_attend.argtypes = [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P, P, P,
-                                C.c_int, I64, I64, I64, I64, I32, C.POINTER(I32), P, P, F, P]
+    protos = {
+        "veda_last_error": (C.c_char_p, []),
+        "veda_version": (C.c_char_p, []),
+        "veda_plan_query": (C.c_int, [C.POINTER(Span), I32, I64, C.POINTER(PlanInfo)]),
+        "veda_plan": (C.c_int, [C.POINTER(PlanInfo), P, P, P]),
+        "veda_select_query": (C.c_int, [C.POINTER(PlanInfo), Budget, Budget, I32, I32,
+                                        C.POINTER(SelectInfo)]),
+        "veda_select": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P,
+                                  C.c_int, I64, I64, I32, C.POINTER(I32), P, P, P, P, P, I32, P,
+                                  SZ, P]),
+        "veda_attend": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P, P, P,
+                                  C.c_int, I64, I64, I64, I64, I32, C.POINTER(I32), P, P, F, P]),
+        "veda_attend_check": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P,
+                                        P, P, C.c_int, I64, I64, I64, I64, I32, C.POINTER(I32),
+                                        P, P]),
+    }
+    for name, (res, args) in protos.items():
+        if hasattr(lib, name):
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+    if not hasattr(lib, "veda_attend"):   # host-only build: no launching entry points
+        lib = _HostOnly(lib)
     _lib = lib
     return lib

@@ -69,5 +69,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZED_HOST_LIB = os.path.join(BUILD, "libveda_host_sanitized.so")
+
+
+def build_host_sanitized() -> str:
+    """The host-only part of libveda (span checks, boxes, budgets, CSR sizing,
+    the attend checks: csrc/host.cpp and csrc/api_host.cpp) as its own shared
+    library, built with g++ under AddressSanitizer and UndefinedBehavior-
+    Sanitizer. It holds no kernel and no launching entry point; tests load it
+    with the ASan runtime preloaded to run the host logic under the sanitizers."""
+    gxx = shutil.which("g++") or "g++"
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [os.path.join(CSRC, n) for n in ("host.cpp", "api_host.cpp")]
+    tmp = SANITIZED_HOST_LIB + ".tmp"
+    _run([gxx, *HOST_FLAGS, "-O1", "-g", "-fno-omit-frame-pointer",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-shared", *srcs,
+          "-o", tmp])
+    os.replace(tmp, SANITIZED_HOST_LIB)
+    return SANITIZED_HOST_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

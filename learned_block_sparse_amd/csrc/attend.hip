@@ -12,12 +12,16 @@
 //   lane 32 apart, and the probabilities, converted to bf16, are already laid
 //   out as the B operand of O^T += V^T P^T. Details at the kernel.
 // f32 kernel (vector ALU): 2 threads per query row, keys in chunks of 32.
+#include <hip/hip_runtime.h>
+
 #include "kernels.hpp"
 
 namespace veda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Dispatch order: the heavy global query tiles (they see every tile) first,
 // then the video tiles. Video tiles are remapped so that each of the 8 XCDs
@@ -195,7 +199,14 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY;
+  // Row sums add, in fp32, exactly the bf16-rounded probabilities the P V
+  // product uses (v_dot2_f32_bf16 of each packed pair with (1, 1)), so the
+  // numerator and the denominator of the softmax agree: a probability's
+  // rounding then moves both alike. They are accumulated in the P V
+  // half-phase, four partial sums per lane over this lane's keys; lanes l and
+  // l + 32 hold the two halves of query l % 32's keys.
+  float racc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
   const int32_t t_begin = a.row_offsets[tile], t_end = a.row_offsets[tile + 1];
   const const_i32 *list = as_const(a.cols + int64_t(hi) * a.entries_per_head);
@@ -303,25 +314,22 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
       }
   };
   // probabilities of keys 8h .. 8h+7 of block kb (in the S^T layout)
-  float racc[4];   // this tile's row sum, four partial sums
   auto exps8 = [&](int kb, int h) {
 #pragma unroll
     for (int i = 8 * h; i < 8 * h + 8; ++i) {
-      const float x = fmaf(s[kb][i], a.scale_log2, -m_run);
-      s[kb][i] = x;   // kept for a recompute against a raised m_run
-      const float p = __builtin_amdgcn_exp2f(x);
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -m_run));
       pb[kb][h][i % 8] = static_cast<__bf16>(p);
-      racc[i & 3] += p;
     }
   };
   // The row's reference value m_run (log2 units) is any value the
   // probabilities exp2(scale s - m_run) stay finite against: softmax is the
   // same for every choice, and bf16 and fp32 keep their relative precision at
   // any magnitude. It is set to the first tile's row max and raised only when
-  // a tile's probabilities sum past 2^20 (or overflow); that tile is then
-  // recomputed against the exact running max, with O and the row sum scaled
-  // to match. Every tile's sum stays <= 2^20, so O and the row sum stay far
-  // inside fp32 range.
+  // a later tile's row max passes it by more than RAISE (then O and the row
+  // sums are scaled down to the new value before that tile's probabilities
+  // are formed). So every probability stays <= 2^RAISE and O and the row sums
+  // stay far inside fp32 range.
+  constexpr float RAISE = 20.0f;
   auto s_max = [&]() {
     float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -330,15 +338,15 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
       for (int i = 0; i < 16; ++i) mx4[i & 3] = fmaxf(mx4[i & 3], s[kb][i]);
     return pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
   };
-  auto tile_sum = [&]() { return pair_sum((racc[0] + racc[1]) + (racc[2] + racc[3])); };
 
   // Schedule. Each group's work per kept tile t is cut into four
   // half-phases, each closed by a workgroup barrier:
-  //   A: softmax(t) first part (mask, probabilities of keys 0..31), loads
-  //      of K(t+1) spread through it
-  //   B: softmax(t) rest (probabilities of keys 32..127, row sum, the rare
-  //      recompute against a raised reference value)
-  //   C: P(t) V(t), each MFMA's transposing V reads issued four MFMAs ahead
+  //   A: softmax(t) first part (mask, row max and the rare raise of the
+  //      reference value, probabilities of keys 0..31), loads of K(t+1)
+  //      spread through it
+  //   B: softmax(t) rest (probabilities of keys 32..127)
+  //   C: P(t) V(t) and the row sums, each MFMA's transposing V reads issued
+  //      four MFMAs ahead
   //   D: S(t+1) = K(t+1) Q^T, reads one k step ahead, loads of V(t+1) spread
   //      through it
   // The two groups run two half-phases apart (the group on waves 0-3 behind),
@@ -398,8 +406,22 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + 8 * (i / 4) + (i % 4) >= thr) s[kb][i] = -INFINITY;
     }
-    if (t == 0) m_run = s_max() * a.scale_log2;   // O and the row sum are still zero
-    racc[0] = racc[1] = racc[2] = racc[3] = 0.0f;
+    {
+      const float xm = s_max() * a.scale_log2;   // this tile's row max, log2 units
+      if (t == 0) {
+        m_run = xm;   // O and the row sums are still zero
+      } else if (__builtin_amdgcn_ballot_w64(xm > m_run + RAISE) != 0) {   // rare
+        const float d = fmaxf(0.0f, xm - m_run);
+        const float alpha = __builtin_amdgcn_exp2f(-d);
+        m_run += d;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) racc[i] *= alpha;
+      }
+    }
     // K(t+1) streams in between chunks of probabilities, a few loads at a
     // time, so no wave waits on the address unit's queue.
 #pragma unroll
@@ -418,37 +440,6 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
     exps8(2, 1);
     exps8(3, 0);
     exps8(3, 1);
-    // the packed probabilities exist here (not sunk past the branch below,
-    // which would keep their fp32 sources live across it)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pb[kb][h]));
-    float ts = tile_sum();
-    if (__builtin_amdgcn_ballot_w64(!(ts <= 0x1p20f)) != 0) {   // rare; also catches inf and NaN
-      // s now holds scale s - m_run: raise m_run by the excess d
-      const float d = fmaxf(0.0f, s_max());
-      if (d > 0.0f) {
-        const float alpha = __builtin_amdgcn_exp2f(-d);
-        m_run += d;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      }
-      racc[0] = racc[1] = racc[2] = racc[3] = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[kb][i] - d);
-          pb[kb][i / 8][i % 8] = static_cast<__bf16>(p);
-          racc[i & 3] += p;
-        }
-      ts = tile_sum();
-    }
-    l_run += ts;
     barrier_vm<NL>();   // V(t) landed in every wave (K(t+1) may not)
     const Rows Rv = rows_of(j1);
     __builtin_amdgcn_s_setprio(1);   // MFMA half-phases issue first
@@ -479,12 +470,20 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
                                                               hi4[0], hi4[1], hi4[2], hi4[3]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8),
                                                        pb[kb][e], o[db], 0, 0, 0);
+        if (db == C::DB - 1) {   // the k step's probabilities into the row sums
+          const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            racc[jj] = __builtin_amdgcn_fdot2_f32_bf16(
+                bf16x2{pb[kb][e][2 * jj], pb[kb][e][2 * jj + 1]}, one, racc[jj], false);
+        }
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA_PV, 0);
 #pragma unroll
       for (int j = 0; j < NM; ++j) {
         if (j + LA_PV < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j % C::DB == C::DB - 1) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
     }
     barrier_vm<NL>();   // K(t+1) landed; every wave is done with V(t)
@@ -505,6 +504,7 @@ __device__ __attribute__((always_inline)) inline void attend_group(const AttendA
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
+  const float l_run = pair_sum((racc[0] + racc[1]) + (racc[2] + racc[3]));
   if (qrow < 0 || shadow) return;
   const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   uint16_t *ob = static_cast<uint16_t *>(a.out) + int64_t(qrow) * a.out_stride_s +

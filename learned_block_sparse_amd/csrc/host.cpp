@@ -3,6 +3,8 @@
 // and row patterns come out bit-identical to it; build with -ffp-contract=off.
 #include "host.hpp"
 
+#include "kernels.hpp"
+
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
@@ -73,7 +75,7 @@ veda_status plan_query(const veda_span *spans, int32_t n_spans, int64_t seq_len,
                        veda_plan_info *info) {
   if (!info) return fail(VEDA_ERR_INVALID, "veda_plan_query: info is NULL");
   std::memset(info, 0, sizeof(*info));
-  if (n_spans <= 0 || !spans) return fail(VEDA_ERR_INVALID, "the target span must be tiled (no spans given)");
+  if (n_spans <= 0 || !spans) return fail(VEDA_ERR_INVALID, "no video span given: the generated video must be tiled");
   if (n_spans > VEDA_MAX_SPANS)
     return fail(VEDA_ERR_INVALID, "more than " + std::to_string(VEDA_MAX_SPANS) + " spans");
   if (seq_len <= 0 || seq_len > INT32_MAX)
@@ -87,8 +89,10 @@ veda_status plan_query(const veda_span *spans, int32_t n_spans, int64_t seq_len,
         return fail(VEDA_ERR_INVALID, "span " + std::to_string(i) + ": grid sides must be positive");
     int64_t rows = int64_t(s.grid[0]) * s.grid[1] * s.grid[2];
     if (s.start < stop || s.start < 0 || s.start + rows > seq_len)
-      return fail(VEDA_ERR_INVALID, "span at " + std::to_string(s.start) +
-                                        " overlaps another or runs past " + std::to_string(seq_len));
+      return fail(VEDA_ERR_INVALID, "video span [" + std::to_string(s.start) + ", " +
+                                        std::to_string(s.start + rows) +
+                                        ") is out of packed order or outside the sequence of " +
+                                        std::to_string(seq_len) + " rows");
     if (s.shape[0] == 0 && s.shape[1] == 0 && s.shape[2] == 0) {
       least_padding_shape(s.grid, s.shape);
     } else if (!is_box(s.shape)) {
@@ -261,6 +265,101 @@ SelectWorkspace select_workspace(const veda_plan_info *info, int32_t D, int32_t 
   w.score_bytes = align256(size_t(H) * nv * nv * sizeof(double));
   w.total = w.score_off + w.score_bytes;
   return w;
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+veda_status check_info(const veda_plan_info *info) {
+  if (!info || info->n_spans <= 0 || info->n_spans > VEDA_MAX_SPANS || info->n_video <= 0 ||
+      info->n_tiles < info->n_video)
+    return fail(VEDA_ERR_INVALID, "plan info is empty or corrupt (call veda_plan_query)");
+  return VEDA_OK;
+}
+
+// Tensors the kernels read 16 bytes at a time: base and both strides must keep
+// every row 16-byte aligned.
+veda_status check_tensor(const void *p, veda_dtype dt, int64_t ss, int64_t sh, const char *name) {
+  if (!p) return fail(VEDA_ERR_INVALID, std::string(name) + " is NULL");
+  const int64_t elt = dt == VEDA_BF16 ? 2 : 4;
+  if (!aligned16(p) || (ss * elt) % 16 != 0 || (sh * elt) % 16 != 0)
+    return fail(VEDA_ERR_UNSUPPORTED,
+                std::string(name) + ": base and strides must be 16-byte aligned");
+  return VEDA_OK;
+}
+
+veda_status fill_heads(const int32_t *heads, int32_t n_heads, int32_t n_heads_total,
+                       HeadList *hl) {
+  if (!heads) return fail(VEDA_ERR_INVALID, "heads is NULL");
+  if (n_heads <= 0 || n_heads > VEDA_MAX_HEADS)
+    return fail(VEDA_ERR_INVALID, "n_heads out of range");
+  std::memset(hl, 0, sizeof(*hl));
+  for (int i = 0; i < n_heads; ++i) {
+    if (heads[i] < 0 || heads[i] >= n_heads_total)
+      return fail(VEDA_ERR_INVALID, "head index " + std::to_string(heads[i]) + " not in [0, " +
+                                        std::to_string(n_heads_total) + ")");
+    hl->h[i] = heads[i];
+  }
+  return VEDA_OK;
+}
+
+veda_status attend_prepare(const veda_plan_info *info, const veda_select_info *sel,
+                           const int32_t *perm, const int32_t *valid_count, const void *q,
+                           const void *k, const void *v, void *out, veda_dtype dtype,
+                           int64_t stride_s, int64_t stride_h, int64_t out_stride_s,
+                           int64_t out_stride_h, int32_t n_heads_total, const int32_t *heads,
+                           const int32_t *row_offsets, const int32_t *cols, float scale,
+                           AttendArgs *a, HeadList *hl) {
+  veda_status st = check_info(info);
+  if (st != VEDA_OK) return st;
+  if (!sel || sel->n_blocks <= 0)
+    return fail(VEDA_ERR_INVALID, "select info is empty (call veda_select_query)");
+  if (!perm || !valid_count || !row_offsets || !cols)
+    return fail(VEDA_ERR_INVALID, "perm / valid_count / row_offsets / cols is NULL");
+  if (dtype != VEDA_F32 && dtype != VEDA_BF16) return fail(VEDA_ERR_INVALID, "unknown dtype");
+  const int D = sel->head_dim;
+  if (D != 64 && D != 128) return fail(VEDA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if ((st = check_tensor(q, dtype, stride_s, stride_h, "q")) != VEDA_OK) return st;
+  if ((st = check_tensor(k, dtype, stride_s, stride_h, "k")) != VEDA_OK) return st;
+  if ((st = check_tensor(v, dtype, stride_s, stride_h, "v")) != VEDA_OK) return st;
+  if ((st = check_tensor(out, dtype, out_stride_s, out_stride_h, "out")) != VEDA_OK) return st;
+  st = fill_heads(heads, sel->n_heads, n_heads_total, hl);
+  if (st != VEDA_OK) return st;
+  // K/V rows are read with 32-bit offsets from each head's first element.
+  const int64_t elt = dtype == VEDA_BF16 ? 2 : 4;
+  const int64_t kv_extent = ((info->seq_len - 1) * stride_s + D) * elt;
+  if (dtype == VEDA_BF16 && kv_extent > int64_t(0xE0000000))
+    return fail(VEDA_ERR_UNSUPPORTED, "q/k/v rows of one head span more than 3.5 GiB");
+  // Row offsets are formed as row * pitch + chunk with 24-bit factors; a
+  // padding slot is read as row seq_len, which must fall past the range above
+  // (rows may not overlap) and still fit in 32 bits.
+  if (dtype == VEDA_BF16 && (stride_s < D || stride_s * 2 >= (int64_t(1) << 24) ||
+                             info->seq_len >= (int64_t(1) << 24) ||
+                             (info->seq_len + 1) * stride_s * 2 > int64_t(0xFFFFFFFF)))
+    return fail(VEDA_ERR_UNSUPPORTED,
+                "bf16 attend needs D <= stride_s < 2^23 elements and seq_len < 2^24 rows");
+  if (!(scale > 0.0f)) scale = float(1.0 / std::sqrt(double(D)));
+  std::memset(a, 0, sizeof(*a));
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->out = out;
+  a->stride_s = stride_s;
+  a->stride_h = stride_h;
+  a->out_stride_s = out_stride_s;
+  a->out_stride_h = out_stride_h;
+  a->perm = perm;
+  a->valid_count = valid_count;
+  a->row_offsets = row_offsets;
+  a->cols = cols;
+  a->entries_per_head = sel->entries_per_head;
+  a->n_heads = sel->n_heads;
+  a->n_tiles = info->n_tiles;
+  a->n_video = info->n_video;
+  a->kv_bytes = uint32_t(kv_extent);
+  a->pad_row = uint32_t(info->seq_len);
+  a->scale = scale;
+  a->scale_log2 = float(double(scale) * 1.4426950408889634);
+  return VEDA_OK;
 }
 
 }  // namespace veda

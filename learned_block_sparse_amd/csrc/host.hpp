@@ -10,6 +10,9 @@
 
 namespace veda {
 
+struct AttendArgs;
+struct HeadList;
+
 // Thread-local text behind veda_last_error().
 void set_error(const std::string &msg);
 void clear_error();
@@ -51,5 +54,22 @@ struct SelectWorkspace {
   size_t total;
 };
 SelectWorkspace select_workspace(const veda_plan_info *info, int32_t head_dim, int32_t n_heads);
+
+// Checks shared by the entry points (host only, no device access).
+veda_status check_info(const veda_plan_info *info);
+veda_status check_tensor(const void *p, veda_dtype dt, int64_t stride_s, int64_t stride_h,
+                         const char *name);
+veda_status fill_heads(const int32_t *heads, int32_t n_heads, int32_t n_heads_total,
+                       HeadList *hl);
+
+// Every check veda_attend makes, in order; on VEDA_OK fills the kernel
+// arguments (veda_attend launches them, veda_attend_check discards them).
+veda_status attend_prepare(const veda_plan_info *info, const veda_select_info *sel,
+                           const int32_t *perm, const int32_t *valid_count, const void *q,
+                           const void *k, const void *v, void *out, veda_dtype dtype,
+                           int64_t stride_s, int64_t stride_h, int64_t out_stride_s,
+                           int64_t out_stride_h, int32_t n_heads_total, const int32_t *heads,
+                           const int32_t *row_offsets, const int32_t *cols, float scale,
+                           AttendArgs *a, HeadList *hl);
 
 }  // namespace veda

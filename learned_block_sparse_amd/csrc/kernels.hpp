@@ -3,7 +3,7 @@
 
 #include <cstdint>
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include "veda.h"
 

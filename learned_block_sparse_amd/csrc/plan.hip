@@ -9,6 +9,8 @@
 // (q / (rh*rw), (q / rw) % rh, q % rw) inside the box. Every box holds its
 // origin cell, so no tile is empty. Global rows (covered by no span) are the
 // gaps between spans, enumerated in ascending order.
+#include <hip/hip_runtime.h>
+
 #include "kernels.hpp"
 
 namespace veda {

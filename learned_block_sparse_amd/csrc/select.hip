@@ -12,6 +12,8 @@
 //                     order-preserving 64-bit keys, ties to the lower column,
 //                     then the kept columns written in ascending order with
 //                     the global tiles after them (the CSR tile list).
+#include <hip/hip_runtime.h>
+
 #include "kernels.hpp"
 
 namespace veda {

@@ -14,6 +14,8 @@ source pages), section by section:
   attention.py  - exact masked attention over tile order, and textbook dense
                   attention used only to pin it (function reference_attend)
   layer.py      - one layer's composition (section "one layer")
+  plans.py      - tile plans, plan choice, float8 projections (section "tile
+                  plans and the predictor file")
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
 import it. It shares no code with the HIP path (learned_block_sparse_amd/)
@@ -28,4 +30,4 @@ Parity pins: every function here is pinned by tests/test_oracle_*.py against
 invariants, closed forms, hand-derived examples (tests/golden/) and brute
 force. No function is "parity unpinned".
 """
-from . import tiles, budget, predictor, selection, attention, layer  # noqa: F401
+from . import tiles, budget, predictor, selection, attention, layer, plans  # noqa: F401

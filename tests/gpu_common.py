@@ -80,6 +80,20 @@ class GpuGroup:
         return ro, cols
 
 
+def bf16_half_ulp(x):
+    """Half the spacing of bf16 values at |x| (8 significant bits): the most
+    that rounding an exact result to bf16 moves it."""
+    m, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
+    e = np.where(m == 0, -125, e)          # zero: the smallest normal's spacing
+    return np.ldexp(1.0, e - 9)
+
+
+def excess_over_bf16_rounding(got, want):
+    """|got - want| beyond the half ulp that rounding the exact `want` to a
+    bf16 output may already cost; zero for a correctly rounded result."""
+    return np.maximum(0.0, np.abs(got - want) - bf16_half_ulp(want))
+
+
 def oracle_csr(mask):
     off, cols = selection.tile_lists(mask)
     return off, cols
