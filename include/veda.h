@@ -212,6 +212,29 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
                         const int32_t *heads, const int32_t *row_offsets, const int32_t *cols,
                         float scale, hipStream_t stream);
 
+/* ---------------------------------------------- select, no allocation --
+ * For callers that cannot allocate device memory or hand in a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. veda_select in scores_mode 0 (same arguments without scores
+ * and workspace), with its scratch in one fixed device array of
+ * VEDA_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends. The heads of a call are processed in chunks whose
+ * pooled features, projections and logits fit the array (one head of the
+ * 108,448-row headline layer, 870 video tiles, needs about 13 MB). Results
+ * equal veda_select's bit for bit. Allocates nothing (no hipMalloc, no
+ * hipFree). Every call on one GPU shares that GPU's array and leaves its
+ * contents behind; nothing in it needs to start at zero (a call writes
+ * everything it reads). Calls that overlap on one GPU (other streams or
+ * threads) race on the array: serialise them. Errors: as veda_select;
+ * UNSUPPORTED when one head's selection alone needs more than the array. */
+#define VEDA_STATIC_SCRATCH_BYTES (64u << 20)
+veda_status veda_select_static(const veda_plan_info *info, const veda_select_info *sel,
+                               const int32_t *perm, const int32_t *valid_count,
+                               const void *q, const void *k, veda_dtype dtype,
+                               int64_t stride_s, int64_t stride_h, int32_t n_heads_total,
+                               const int32_t *heads, const float *proj_q, const float *proj_k,
+                               int32_t *row_offsets, int32_t *cols, hipStream_t stream);
+
 /* Host only, synchronous: every check veda_attend makes (the arguments, the
  * head list, alignment and the bf16 path's addressing limits), with the same
  * arguments but no scale and no stream, and nothing launched. A layer made of

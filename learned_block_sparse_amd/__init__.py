@@ -18,7 +18,7 @@ from ._lib import Budget, PlanInfo, SelectInfo, Span, TILE
 
 __all__ = ["VedaError", "VedaUnsupported", "VedaDeviceError", "budget", "summary", "receipt",
            "veda_plan_query", "veda_plan", "veda_select_query", "veda_select", "veda_attend",
-           "veda_attend_check", "Plan", "plan", "Policy", "parse_index_list", "attention",
+           "veda_attend_check", "veda_select_static", "Plan", "plan", "Policy", "parse_index_list", "attention",
            "version", "library_path"]
 
 
@@ -179,6 +179,35 @@ def veda_select(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, heads,
         _ptr(q) if scores_mode != 2 else None, _ptr(k) if scores_mode != 2 else None, dt,
         ss, sh, ht, harr, _ptr(proj_q), _ptr(proj_k), _ptr(row_offsets), _ptr(cols),
         _ptr(scores), int(scores_mode), _ptr(workspace), ws_bytes, _stream(stream)))
+    return row_offsets, cols
+
+
+def veda_select_static(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, heads,
+                       proj_q, proj_k, row_offsets=None, cols=None, stream=None):
+    """veda_select (scores_mode 0) without a workspace: the library's fixed
+    device scratch holds the pooled features, projections and logits, a few
+    heads at a time (include/veda.h, veda_select_static). For callers that
+    cannot allocate; pass row_offsets and cols to allocate nothing at all.
+    Calls that overlap on one GPU race on the scratch. Returns
+    (row_offsets, cols)."""
+    import torch
+    dev = perm.device
+    harr, nh = _heads_array(heads)
+    if nh != sel.n_heads:
+        raise VedaError("len(heads) differs from the n_heads given to veda_select_query")
+    if row_offsets is None:
+        row_offsets = torch.empty(info.n_tiles + 1, dtype=torch.int32, device=dev)
+    if cols is None:
+        cols = torch.empty(nh * sel.entries_per_head, dtype=torch.int32, device=dev)
+    _check_qkv(q, k)
+    for p in (proj_q, proj_k):
+        if p is None or p.dtype != torch.float32 or not p.is_contiguous() or \
+                tuple(p.shape) != (nh, 3 * sel.head_dim, sel.head_dim):
+            raise VedaError("proj_q / proj_k must be contiguous float32 [n_heads, 3D, D]")
+    _check(_lib.load().veda_select_static(
+        C.byref(info), C.byref(sel), _ptr(perm), _ptr(valid_count), _ptr(q), _ptr(k),
+        _dtype_code(q), q.stride(0), q.stride(1), q.shape[1], harr, _ptr(proj_q), _ptr(proj_k),
+        _ptr(row_offsets), _ptr(cols), _stream(stream)))
     return row_offsets, cols
 
 

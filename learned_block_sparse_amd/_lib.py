@@ -17,12 +17,14 @@ TILE = 128
 MAX_SPANS = 16
 MAX_BLOCKS = 2
 MAX_HEADS = 256
+STATIC_SCRATCH_BYTES = 64 << 20     # VEDA_STATIC_SCRATCH_BYTES
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_DEVICE = 0, 1, 2, 3
 F32, BF16 = 0, 1
 
 EXPORTS = ("veda_last_error", "veda_version", "veda_plan_query", "veda_plan",
-           "veda_select_query", "veda_select", "veda_attend", "veda_attend_check")
+           "veda_select_query", "veda_select", "veda_attend", "veda_attend_check",
+           "veda_select_static")
 
 
 class Span(C.Structure):
@@ -100,6 +102,8 @@ def load():
                                   SZ, P]),
         "veda_attend": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P, P, P,
                                   C.c_int, I64, I64, I64, I64, I32, C.POINTER(I32), P, P, F, P]),
+        "veda_select_static": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P,
+                                         C.c_int, I64, I64, I32, C.POINTER(I32), P, P, P, P, P]),
         "veda_attend_check": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P,
                                         P, P, C.c_int, I64, I64, I64, I64, I32, C.POINTER(I32),
                                         P, P]),
