@@ -235,6 +235,37 @@ veda_status veda_select_static(const veda_plan_info *info, const veda_select_inf
                                const int32_t *heads, const float *proj_q, const float *proj_k,
                                int32_t *row_offsets, int32_t *cols, hipStream_t stream);
 
+/* ---------------------------------------------------- teacher and recall --
+ * The tile-level teacher map that the news pages name as Veda's training
+ * signal (full attention max-pooled onto the tiles; comfyui-wiki Veda news,
+ * Spanish edition section "Qué hace Veda", French "Ce que fait Veda"), and
+ * the recall of a selection against it. Not on the attention path: for
+ * measuring how much of full attention the kept tiles cover.
+ *
+ * veda_teacher: for head heads[i], query tile a and key tile b,
+ *   teacher[i][a][b] = max over the real rows r of a and the real rows j of b
+ *                      of softmax_j(q_r . k_j * scale), the softmax over every
+ *                      real row of the sequence (full attention).
+ *   q, k    device bf16 [S, H_total, D] (strides in elements), D in {64, 128}.
+ *   heads   HOST int32[n_heads].
+ *   scale   softmax scale; <= 0 means head_dim^-1/2.
+ *   teacher device float[n_heads][n_tiles][n_tiles], written in full.
+ * Dense work: two passes of q.k over every tile pair (4 * 128^2 * D flop per
+ * pair and head). Errors: UNSUPPORTED for f32 inputs or another head_dim.
+ *
+ * veda_recall: recall[i][a] = sum of teacher[i][a][b] over the tiles b in
+ * row a of the CSR tile lists (as veda_select writes them, sel->n_heads
+ * heads) divided by the sum over all b: the share of the teacher's
+ * distribution the selection keeps. recall is device float[n_heads][n_tiles]. */
+veda_status veda_teacher(const veda_plan_info *info, const int32_t *perm,
+                         const int32_t *valid_count, const void *q, const void *k,
+                         veda_dtype dtype, int64_t stride_s, int64_t stride_h,
+                         int32_t n_heads_total, const int32_t *heads, int32_t n_heads,
+                         int32_t head_dim, float scale, float *teacher, hipStream_t stream);
+veda_status veda_recall(const veda_plan_info *info, const veda_select_info *sel,
+                        const int32_t *row_offsets, const int32_t *cols, const float *teacher,
+                        float *recall, hipStream_t stream);
+
 /* Host only, synchronous: every check veda_attend makes (the arguments, the
  * head list, alignment and the bf16 path's addressing limits), with the same
  * arguments but no scale and no stream, and nothing launched. A layer made of

@@ -18,7 +18,7 @@ from ._lib import Budget, PlanInfo, SelectInfo, Span, TILE
 
 __all__ = ["VedaError", "VedaUnsupported", "VedaDeviceError", "budget", "summary", "receipt",
            "veda_plan_query", "veda_plan", "veda_select_query", "veda_select", "veda_attend",
-           "veda_attend_check", "veda_select_static", "Plan", "plan", "Policy", "parse_index_list", "attention",
+           "veda_attend_check", "veda_select_static", "veda_teacher", "veda_recall", "Plan", "plan", "Policy", "parse_index_list", "attention",
            "version", "library_path"]
 
 
@@ -244,6 +244,41 @@ def veda_attend_check(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, 
         C.byref(info), C.byref(sel), _ptr(perm), _ptr(valid_count), _ptr(q), _ptr(k), _ptr(v),
         _ptr(out), _dtype_code(q), q.stride(0), q.stride(1), out.stride(0), out.stride(1),
         q.shape[1], harr, _ptr(row_offsets), _ptr(cols)))
+
+
+# ---------------------------------------------------- teacher and recall --
+def veda_teacher(info: PlanInfo, perm, valid_count, q, k, heads, head_dim=None, scale=0.0,
+                 teacher=None, stream=None):
+    """The max-pooled full-attention teacher map, float32 [n_heads, n_tiles,
+    n_tiles] on the device (include/veda.h, veda_teacher)."""
+    import torch
+    _check_qkv(q, k)
+    harr, nh = _heads_array(heads)
+    D = q.shape[2] if head_dim is None else int(head_dim)
+    n = info.n_tiles
+    if teacher is None:
+        teacher = torch.empty((nh, n, n), dtype=torch.float32, device=q.device)
+    if teacher.dtype != torch.float32 or not teacher.is_contiguous() or \
+            teacher.numel() < nh * n * n:
+        raise VedaError("teacher must be contiguous float32 [n_heads, n_tiles, n_tiles]")
+    _check(_lib.load().veda_teacher(
+        C.byref(info), _ptr(perm), _ptr(valid_count), _ptr(q), _ptr(k), _dtype_code(q),
+        q.stride(0), q.stride(1), q.shape[1], harr, nh, D, float(scale), _ptr(teacher),
+        _stream(stream)))
+    return teacher
+
+
+def veda_recall(info: PlanInfo, sel: SelectInfo, row_offsets, cols, teacher, recall=None,
+                stream=None):
+    """Per head and query tile, the teacher distribution's share on the tiles
+    of the CSR lists: float32 [n_heads, n_tiles] on the device."""
+    import torch
+    if recall is None:
+        recall = torch.empty((sel.n_heads, info.n_tiles), dtype=torch.float32,
+                             device=teacher.device)
+    _check(_lib.load().veda_recall(C.byref(info), C.byref(sel), _ptr(row_offsets), _ptr(cols),
+                                   _ptr(teacher), _ptr(recall), _stream(stream)))
+    return recall
 
 
 # ------------------------------------------------------------- one layer --

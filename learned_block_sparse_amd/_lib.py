@@ -24,7 +24,7 @@ F32, BF16 = 0, 1
 
 EXPORTS = ("veda_last_error", "veda_version", "veda_plan_query", "veda_plan",
            "veda_select_query", "veda_select", "veda_attend", "veda_attend_check",
-           "veda_select_static")
+           "veda_select_static", "veda_teacher", "veda_recall")
 
 
 class Span(C.Structure):
@@ -104,6 +104,9 @@ def load():
                                   C.c_int, I64, I64, I64, I64, I32, C.POINTER(I32), P, P, F, P]),
         "veda_select_static": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P,
                                          C.c_int, I64, I64, I32, C.POINTER(I32), P, P, P, P, P]),
+        "veda_teacher": (C.c_int, [C.POINTER(PlanInfo), P, P, P, P, C.c_int, I64, I64, I32,
+                                   C.POINTER(I32), I32, I32, F, P, P]),
+        "veda_recall": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P, P]),
         "veda_attend_check": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P,
                                         P, P, C.c_int, I64, I64, I64, I64, I32, C.POINTER(I32),
                                         P, P]),

@@ -217,3 +217,61 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
 }
 
 }  // extern "C"
+
+extern "C" {
+
+veda_status veda_teacher(const veda_plan_info *info, const int32_t *perm,
+                         const int32_t *valid_count, const void *q, const void *k,
+                         veda_dtype dtype, int64_t stride_s, int64_t stride_h,
+                         int32_t n_heads_total, const int32_t *heads, int32_t n_heads,
+                         int32_t head_dim, float scale, float *teacher, hipStream_t stream) {
+  veda_status st = check_info(info);
+  if (st != VEDA_OK) return st;
+  if (!perm || !valid_count || !teacher)
+    return fail(VEDA_ERR_INVALID, "perm / valid_count / teacher is NULL");
+  if (dtype != VEDA_BF16) return fail(VEDA_ERR_UNSUPPORTED, "the teacher map takes bf16 q and k");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(VEDA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if ((st = check_tensor(q, dtype, stride_s, stride_h, "q")) != VEDA_OK) return st;
+  if ((st = check_tensor(k, dtype, stride_s, stride_h, "k")) != VEDA_OK) return st;
+  if (stride_s < head_dim) return fail(VEDA_ERR_UNSUPPORTED, "rows narrower than head_dim");
+  HeadList hl;
+  if ((st = fill_heads(heads, n_heads, n_heads_total, &hl)) != VEDA_OK) return st;
+  if (int64_t(n_heads) * info->n_tiles * info->n_tiles > (int64_t(1) << 40))
+    return fail(VEDA_ERR_UNSUPPORTED, "teacher map too large");
+  if (!(scale > 0.0f)) scale = float(1.0 / std::sqrt(double(head_dim)));
+  TeacherArgs a;
+  a.q = q;
+  a.k = k;
+  a.stride_s = stride_s;
+  a.stride_h = stride_h;
+  a.perm = perm;
+  a.valid_count = valid_count;
+  a.teacher = teacher;
+  a.n_heads = n_heads;
+  a.n_tiles = info->n_tiles;
+  a.scale_log2 = float(double(scale) * 1.4426950408889634);
+  return device_status(launch_teacher(a, hl, head_dim, stream), "teacher launch");
+}
+
+veda_status veda_recall(const veda_plan_info *info, const veda_select_info *sel,
+                        const int32_t *row_offsets, const int32_t *cols, const float *teacher,
+                        float *recall, hipStream_t stream) {
+  veda_status st = check_info(info);
+  if (st != VEDA_OK) return st;
+  if (!sel || sel->n_blocks <= 0)
+    return fail(VEDA_ERR_INVALID, "select info is empty (call veda_select_query)");
+  if (!row_offsets || !cols || !teacher || !recall)
+    return fail(VEDA_ERR_INVALID, "row_offsets / cols / teacher / recall is NULL");
+  RecallArgs a;
+  a.teacher = teacher;
+  a.row_offsets = row_offsets;
+  a.cols = cols;
+  a.entries_per_head = sel->entries_per_head;
+  a.recall = recall;
+  a.n_heads = sel->n_heads;
+  a.n_tiles = info->n_tiles;
+  return device_status(launch_recall(a, stream), "recall launch");
+}
+
+}  // extern "C"

@@ -89,4 +89,25 @@ hipError_t launch_attend_bf16(const AttendArgs &a, const HeadList &heads, int he
 hipError_t launch_attend_f32(const AttendArgs &a, const HeadList &heads, int head_dim,
                              hipStream_t s);
 
+// -------------------------------------------------------------- teacher --
+struct TeacherArgs {
+  const void *q, *k;          // bf16 [S, H, D] rows
+  int64_t stride_s, stride_h;
+  const int32_t *perm, *valid_count;
+  float *teacher;             // [n_heads][n_tiles][n_tiles]
+  int32_t n_heads, n_tiles;
+  float scale_log2;           // softmax scale * log2(e)
+};
+hipError_t launch_teacher(const TeacherArgs &a, const HeadList &heads, int head_dim,
+                          hipStream_t s);
+
+struct RecallArgs {
+  const float *teacher;       // [n_heads][n_tiles][n_tiles]
+  const int32_t *row_offsets, *cols;
+  int64_t entries_per_head;
+  float *recall;              // [n_heads][n_tiles]
+  int32_t n_heads, n_tiles;
+};
+hipError_t launch_recall(const RecallArgs &a, hipStream_t s);
+
 }  // namespace veda

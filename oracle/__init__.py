@@ -14,6 +14,8 @@ source pages), section by section:
   attention.py  - exact masked attention over tile order, and textbook dense
                   attention used only to pin it (function reference_attend)
   layer.py      - one layer's composition (section "one layer")
+  teacher.py    - the max-pooled full-attention teacher map and recall (news
+                  pages, the method's training signal)
   plans.py      - tile plans, plan choice, float8 projections (section "tile
                   plans and the predictor file")
 
@@ -30,4 +32,4 @@ Parity pins: every function here is pinned by tests/test_oracle_*.py against
 invariants, closed forms, hand-derived examples (tests/golden/) and brute
 force. No function is "parity unpinned".
 """
-from . import tiles, budget, predictor, selection, attention, layer, plans  # noqa: F401
+from . import tiles, budget, predictor, selection, attention, layer, plans, teacher  # noqa: F401

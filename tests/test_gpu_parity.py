@@ -415,3 +415,38 @@ def test_full_attention_policy_runs_keep_all_kernels():
         assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
     assert stats["dense_calls"] == 1 and stats.get("sparse_calls", 0) == 0
     assert veda.summary(stats).startswith("Attention computed: 100.0%")
+
+
+@pytest.mark.parametrize("name", ["padding", "refs_whole", "ragged_refs", "mid"])
+def test_teacher_map_and_recall(name):
+    """The max-pooled full-attention teacher map and the recall of the
+    selected tile lists against the oracle (oracle/teacher.py): the map
+    within 1e-4 relative (fp32 softmax statistics over bf16 inputs), the
+    recall within 1e-4. Small layouts compare every query tile; mid a seeded
+    sample plus the last tile."""
+    from oracle import teacher as oteacher
+    inp, dev, groups = _make(name)
+    for g in groups:
+        gg = GpuGroup(inp, dev, g.shape, g.heads, scores_mode=2, oracle_scores=g.scores)
+        log(f"[teacher] {name} shape={g.shape} tiles={gg.info.n_tiles}")
+        T = veda.veda_teacher(gg.info, gg.perm, gg.vc, dev["q"], dev["k"], g.heads)
+        rec = veda.veda_recall(gg.info, gg.sel, gg.row_offsets, gg.cols, T)
+        torch.cuda.synchronize()
+        lay = g.layout
+        qt = None if lay.n_tiles <= 64 else \
+            np.unique(np.append(workloads.sample_tiles(lay.n_tiles, 6, seed=11), lay.n_tiles - 1))
+        want = oteacher.teacher_map(inp.q, inp.k, lay, g.heads, query_tiles=qt)
+        got = T.cpu().numpy().astype(np.float64)
+        got = got if qt is None else got[:, qt]
+        rel = np.abs(got - want) / np.maximum(want, 1e-30)
+        log(f"[teacher] {name} max rel err {rel.max():.2e}")
+        assert (np.abs(got - want) <= 1e-4 * want + 1e-12).all()
+        mask = g.mask if qt is None else g.mask[:, qt]
+        r_want = oteacher.recall(want, mask)
+        r_got = rec.cpu().numpy().astype(np.float64)
+        r_got = r_got if qt is None else r_got[:, qt]
+        log(f"[teacher] {name} recall mean {r_got.mean():.4f} (oracle {r_want.mean():.4f})")
+        assert np.abs(r_got - r_want).max() <= 1e-4
+        nv = lay.n_video
+        if nv < lay.n_tiles and qt is None:
+            assert np.allclose(r_got[:, nv:], 1.0, atol=1e-5)   # global rows keep every tile
