@@ -18,6 +18,8 @@ source pages), section by section:
                   pages, the method's training signal)
   plans.py      - tile plans, plan choice, float8 projections (section "tile
                   plans and the predictor file")
+  int8.py       - attention with int8 q.k products: the approximate arithmetic
+                  the news pages name for Veda's kernel, in a stated reading
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
 import it. It shares no code with the HIP path (learned_block_sparse_amd/)
@@ -26,10 +28,12 @@ arithmetic of the method.
 
 Precision: everything floating is fp64. The pages compute pooling and logits
 in fp32 with an unspecified reduction order; fp64 is taken on both sides so
-that the top-k decisions agree bit for bit (readings).
+that the top-k decisions agree bit for bit. The one exception is int8.py's
+quantiser: its codes are integers decided by floating point, decided in fp32
+as the device decides them.
 
 Parity pins: every function here is pinned by tests/test_oracle_*.py against
 invariants, closed forms, hand-derived examples (tests/golden/) and brute
 force. No function is "parity unpinned".
 """
-from . import tiles, budget, predictor, selection, attention, layer, plans, teacher  # noqa: F401
+from . import tiles, budget, predictor, selection, attention, layer, plans, teacher, int8  # noqa: F401

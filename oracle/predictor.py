@@ -1,7 +1,8 @@
 """Triplet pooling and tile-pair logits (oracle; test infrastructure only).
 
 Follows `veda_core.py` (page 1), section "predictor": pool() and logits().
-fp64 throughout (the pages use fp32; see the precision reading in the design doc).
+fp64 throughout. The pages use fp32 with an unstated reduction order; fp64 on
+both sides lets the top-k decisions agree bit for bit.
 """
 from __future__ import annotations
 

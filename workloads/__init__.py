@@ -10,7 +10,7 @@ The five workloads mirror the shapes the Veda pages quote: a 104k-token
 layer comparable to 1344x768 at 124 frames (the headline), a 720p 241-frame
 clip with per-head tile shapes, and three smaller cases. The pages measure on
 real MiniMax H3 / Waver activations, which are not available; these synthetic
-tensors stand in for them (see the input recipe in the design doc).
+tensors stand in for them, by the recipe below.
 
 Recipe (per workload, seed ``1000 + index``, numpy PCG64):
   1. q, k, v: float32 standard normal, shape [S, H, D]. Rows are drawn in
