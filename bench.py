@@ -1,6 +1,7 @@
 """Benchmark of one Veda attention layer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload headline] [--no-cpu]
+                    [--qk bf16|int8]
 
 A step is the whole hot path over the layer: plan (tile packing), select
 (pooling, fp64 tile logits, top-k -> CSR tile lists) and attend (tile-skip
@@ -12,6 +13,11 @@ stream the kernels run on. Prints one JSON line:
   cpu_baseline the CPU oracle on a bounded sample of the same layer, scaled
 plus context: attend TFLOP/s over real rows only, and the vendor library's
 bf16 GEMM rate measured in the same run (the practical MFMA ceiling).
+
+--qk int8 runs the attend stage with int8 q.k products (veda_attend_int8:
+K quantisation pre-pass + attend); its roofline peak is the mixed MFMA rate
+of that kernel's work, half its flops in int8 and half (P V) in bf16. A bf16
+run also times the int8 attend call alone on the same layer ("int8_qk").
 """
 from __future__ import annotations
 
@@ -30,6 +36,9 @@ if ROOT not in sys.path:
 METRIC = "kept-tile attention TFLOP/s & ms/layer at 104k tokens, 90% sparse; % MFMA peak"
 BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense bf16 MFMA)
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 2 * BF16_PEAK_TFLOPS   # dense int8 MFMA: twice the bf16 rate
+# Q K^T (half the attend flops) at the int8 rate, P V (the other half) at bf16
+MIXED_PEAK_TFLOPS = 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / BF16_PEAK_TFLOPS)
 
 
 def _args():
@@ -40,6 +49,8 @@ def _args():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--qk", choices=("bf16", "int8"), default="bf16",
+                    help="q.k products of the attend stage: bf16 (default) or int8")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run two device copies of MIB MiB (the known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -50,22 +61,27 @@ def _args():
 # this file (see it for the commands and the copy-kernel calibration). It is
 # reported only while the kernel source is the one the counters were taken on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_headline_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "learned_block_sparse_amd", "csrc", n)
-                  for n in ("attend.hip", "kernels.hpp")]
+_CSRC = os.path.join(ROOT, "learned_block_sparse_amd", "csrc")
+KERNEL_SOURCES = {
+    "bf16": ("attend.hip", "attend_common.hpp", "kernels.hpp"),
+    "int8": ("attend_i8.hip", "attend_i8.hpp", "attend_common.hpp", "kernels.hpp"),
+}
+KERNEL_NAMES = {"bf16": "attend_bf16_kernel<128>", "int8": "attend_i8_kernel<128>"}
 
 
-def _kernel_digest():
+def _kernel_digest(qk):
     import hashlib
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
+    for name in KERNEL_SOURCES[qk]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def _recorded_traffic(workload):
+def _recorded_traffic(workload, qk="bf16"):
     """Bytes per attend launch from the recorded counters, or None when the
-    record is missing, for another workload, or for another kernel source."""
+    record is missing, for another workload or kernel, or for another kernel
+    source."""
     import re
     try:
         with open(TRAFFIC_FILE) as f:
@@ -74,7 +90,8 @@ def _recorded_traffic(workload):
         return None
     for m in re.finditer(r"<!-- traffic (\{.*?\}) -->", text):
         rec = json.loads(m.group(1))
-        if rec.get("workload") == workload and rec.get("kernel_sha256") == _kernel_digest():
+        if rec.get("workload") == workload and rec.get("kernel") == KERNEL_NAMES[qk] and \
+                rec.get("kernel_sha256") == _kernel_digest(qk):
             return float(rec["bytes_per_launch"])
     return None
 
@@ -134,6 +151,8 @@ class Layer:
                      ro=torch.empty(info.n_tiles + 1, dtype=torch.int32, device=dev),
                      cols=torch.empty(len(heads) * sel.entries_per_head, dtype=torch.int32, device=dev),
                      ws=torch.empty(sel.workspace_bytes, dtype=torch.uint8, device=dev),
+                     ws8=torch.empty(veda.veda_attend_int8_query(info, sel), dtype=torch.uint8,
+                                     device=dev) if wl.dtype == "bf16" else None,
                      pq=pq.index_select(0, idx).contiguous(), pk=pk.index_select(0, idx).contiguous())
             self.groups.append(g)
         self.pairs = sum(len(g["heads"]) * g["sel"].entries_per_head for g in self.groups)
@@ -171,6 +190,13 @@ class Layer:
         for g in self.groups:
             v.veda_attend(g["info"], g["sel"], g["perm"], g["vc"], self.t["q"], self.t["k"],
                           self.t["v"], g["heads"], g["ro"], g["cols"], out=self.out)
+
+    def attend_int8(self):
+        v = self.veda
+        for g in self.groups:
+            v.veda_attend_int8(g["info"], g["sel"], g["perm"], g["vc"], self.t["q"], self.t["k"],
+                               self.t["v"], g["heads"], g["ro"], g["cols"], out=self.out,
+                               workspace=g["ws8"])
 
 
 def _gemm_ceiling(n=16384, reps=5):
@@ -269,7 +295,11 @@ def main():
     _log(f"[bench] generating {args.workload}")
     inp = workloads.generate(args.workload)
     wl = inp.workload
+    if args.qk == "int8" and wl.dtype != "bf16":
+        print("--qk int8 takes a bf16 workload", file=sys.stderr)
+        sys.exit(2)
     L = Layer(inp)
+    attend = L.attend_int8 if args.qk == "int8" else L.attend
     _log(f"[bench] kept pairs {L.pairs}, {L.flops / 1e12:.3f} TFLOP per layer")
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -282,7 +312,7 @@ def main():
     plan_cold_ms = e0.elapsed_time(e1)
 
     for _ in range(args.warmup):
-        L.plan(); L.select(); L.attend()
+        L.plan(); L.select(); attend()
     torch.cuda.synchronize()
     _log("[bench] warmup done")
 
@@ -294,7 +324,7 @@ def main():
         m = [ev() for _ in range(4)]
         m[0].record(); L.plan()
         m[1].record(); L.select()
-        m[2].record(); L.attend()
+        m[2].record(); attend()
         m[3].record()
         marks.append(m)
     t_stop.record()
@@ -309,7 +339,29 @@ def main():
          f"{np.median(sel_ms):.3f} attend {np.median(att_ms):.3f}")
 
     attend_tflops = L.flops / (att_avg * 1e-3) / 1e12
+    peak = MIXED_PEAK_TFLOPS if args.qk == "int8" else BF16_PEAK_TFLOPS
     real_flops = L.real_row_flops()
+    int8_leg = None
+    if args.qk == "bf16" and wl.dtype == "bf16":
+        # the int8 attend call alone on the same layer and tile lists
+        L.attend_int8()
+        torch.cuda.synchronize()
+        ms8 = []
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(); L.attend_int8(); b.record()
+            ms8.append((a, b))
+        torch.cuda.synchronize()
+        ms8 = [a.elapsed_time(b) for a, b in ms8]
+        t8 = L.flops / (float(np.mean(ms8)) * 1e-3) / 1e12
+        int8_leg = {
+            "attend_median_ms": float(np.median(ms8)), "attend_tflops": t8,
+            "pct_mixed_peak": 100.0 * t8 / MIXED_PEAK_TFLOPS,
+            "mixed_peak_tflops": MIXED_PEAK_TFLOPS,
+            "note": "veda_attend_int8 (K quantisation + attend) on the same layer; "
+                    "approximate (int8 q.k), not the headline path",
+        }
+        _log(f"[bench] int8 q.k attend {np.median(ms8):.3f} ms ({t8:.0f} TFLOP/s)")
     gemm = _gemm_ceiling()
     _log(f"[bench] bf16 GEMM ceiling {gemm:.1f} TFLOP/s")
     result = {
@@ -323,14 +375,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": "bf16, q.k int8" if args.qk == "int8" else wl.dtype,
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {wl.note}",
             "seq_len": wl.seq_len, "heads": wl.n_heads, "head_dim": wl.head_dim,
             "generated_budget": list(wl.generated), "reference_budget": list(wl.reference),
             "kept_tile_pairs": L.pairs, "tflop_per_layer": L.flops / 1e12,
-            "parallelism": "single GPU",
+            "parallelism": "single GPU", "qk": args.qk,
         },
         "stages_ms": {
             "plan_cold": plan_cold_ms,
@@ -342,13 +394,14 @@ def main():
         },
         "attend_tflops": attend_tflops,
         "attend_pct_bf16_peak": 100.0 * attend_tflops / BF16_PEAK_TFLOPS,
+        "int8_qk": int8_leg,
         "attend_real_row_tflops": real_flops / (att_avg * 1e-3) / 1e12,
         "gemm_ceiling_tflops": gemm,
         "attend_pct_gemm_ceiling": 100.0 * attend_tflops / gemm,
         "roofline": {
-            "bound": "mfma", "achieved": attend_tflops, "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": attend_tflops / BF16_PEAK_TFLOPS,
-            "traffic": _recorded_traffic(wl.name),
+            "bound": "mfma", "achieved": attend_tflops, "peak": peak,
+            "unit": "TFLOP/s", "frac": attend_tflops / peak,
+            "traffic": _recorded_traffic(wl.name, args.qk),
         },
         "cpu_baseline": None,
     }

@@ -212,6 +212,40 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
                         const int32_t *heads, const int32_t *row_offsets, const int32_t *cols,
                         float scale, hipStream_t stream);
 
+/* ---------------------------------------------------- attend, int8 Q.K^T --
+ * veda_attend with the q.k products in int8, the approximate arithmetic the
+ * news pages name for Veda's own kernel (an INT8 kernel, comfyui-wiki Veda
+ * news, "Rendimiento" / "Performances"; the Vflash guide notes it gives no
+ * exact-arithmetic guarantee). Same arguments and result as veda_attend
+ * with bf16 q, k, v, out, up to the quantisation:
+ *   key tile j of head heads[i]: s_k = max |k| over the tile's real rows
+ *     divided by 127, codes rint(k / s_k) (round half to even), int8;
+ *   query row r: s_q = max |q_r| / 127, codes rint(q_r / s_q);
+ *   logit = (integer dot of the codes) * s_q * s_k * scale.
+ * An all-zero row or tile has scale 0 and logits exactly 0. Probabilities,
+ * row sums, P.V and the output are as in veda_attend's bf16 path.
+ *   workspace  device scratch of at least the size veda_attend_int8_query
+ *              gives, 16-byte aligned: the int8 codes of K in tile order
+ *              (n_heads x n_tiles x 128 x head_dim bytes) and the per-tile
+ *              scales (n_heads x n_tiles floats). Written in full by the
+ *              call's first kernel, read by its second; nothing in it needs
+ *              to start at zero. Calls that share one workspace on different
+ *              streams race on it.
+ * Errors: those of veda_attend for bf16; INVALID for a NULL or too small
+ * workspace or dtype other than bf16 (there is no dtype argument: q, k, v
+ * and out are bf16); UNSUPPORTED when one head's codes reach 2 GiB.
+ * Asynchronous on `stream`. */
+veda_status veda_attend_int8_query(const veda_plan_info *info, const veda_select_info *sel,
+                                   size_t *workspace_bytes);
+veda_status veda_attend_int8(const veda_plan_info *info, const veda_select_info *sel,
+                             const int32_t *perm, const int32_t *valid_count,
+                             const void *q, const void *k, const void *v, void *out,
+                             int64_t stride_s, int64_t stride_h,
+                             int64_t out_stride_s, int64_t out_stride_h, int32_t n_heads_total,
+                             const int32_t *heads, const int32_t *row_offsets,
+                             const int32_t *cols, float scale, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------- select, no allocation --
  * For callers that cannot allocate device memory or hand in a workspace:
  * code under HIP graph capture, tight serving loops, harnesses that forbid

@@ -18,7 +18,8 @@ from ._lib import Budget, PlanInfo, SelectInfo, Span, TILE
 
 __all__ = ["VedaError", "VedaUnsupported", "VedaDeviceError", "budget", "summary", "receipt",
            "veda_plan_query", "veda_plan", "veda_select_query", "veda_select", "veda_attend",
-           "veda_attend_check", "veda_select_static", "veda_teacher", "veda_recall", "Plan", "plan", "Policy", "parse_index_list", "attention",
+           "veda_attend_check", "veda_select_static", "veda_teacher", "veda_recall",
+           "veda_attend_int8_query", "veda_attend_int8", "Plan", "plan", "Policy", "parse_index_list", "attention",
            "version", "library_path"]
 
 
@@ -232,6 +233,42 @@ def veda_attend(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, v, hea
     return out
 
 
+def veda_attend_int8_query(info: PlanInfo, sel: SelectInfo) -> int:
+    """Bytes of device workspace veda_attend_int8 needs for this layout and
+    head group."""
+    n = C.c_size_t(0)
+    _check(_lib.load().veda_attend_int8_query(C.byref(info), C.byref(sel), C.byref(n)))
+    return int(n.value)
+
+
+def veda_attend_int8(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, v, heads,
+                     row_offsets, cols, out=None, scale=0.0, workspace=None, stream=None):
+    """Tile-skip attention with int8 q.k products (include/veda.h,
+    veda_attend_int8): bf16 q, k, v; writes every row of the listed heads of
+    `out` (allocated if None) and returns it. `workspace`: a device uint8
+    tensor of at least veda_attend_int8_query bytes, allocated if None."""
+    import torch
+    _check_qkv(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise VedaError("veda_attend_int8 takes bf16 q, k, v")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or out.stride(2) != 1:
+        raise VedaError("out must match q's shape and dtype with a contiguous last axis")
+    harr, nh = _heads_array(heads)
+    if nh != sel.n_heads:
+        raise VedaError("len(heads) differs from the n_heads given to veda_select_query")
+    need = veda_attend_int8_query(info, sel)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(_lib.load().veda_attend_int8(
+        C.byref(info), C.byref(sel), _ptr(perm), _ptr(valid_count), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(out), q.stride(0), q.stride(1), out.stride(0), out.stride(1), q.shape[1], harr,
+        _ptr(row_offsets), _ptr(cols), float(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def veda_attend_check(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, v, heads,
                       row_offsets, cols, out):
     """Every check veda_attend makes, on the host, launching nothing; raises
@@ -353,7 +390,7 @@ _KEEP_ALL = ("ratio", 1.0)
 
 def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, reference,
               cache=None, out=None, stats=None, stream=None, fallback=None, layer=None,
-              step=None, policy=None):
+              step=None, policy=None, qk="bf16"):
     """One layer of Veda attention over q, k, v [S, H, D] (bf16 or float32).
 
     refs        : [(start, (T, H, W))] reference video spans (packed order)
@@ -378,6 +415,9 @@ def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, ref
                   is given (the model's own attention), else libveda's
                   kernels with every tile kept, which is exact dense
                   attention. It counts as a dense call in the receipt.
+    qk          : "bf16" (default) or "int8": the q.k products of sparse
+                  calls in int8 (veda_attend_int8; bf16 q, k, v only). Dense
+                  calls keep bf16 products.
 
     References are tiled with their least-padding box unless the reference
     budget keeps everything, in which case their rows stay global (dense).
@@ -393,7 +433,8 @@ def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, ref
             res = _into(out, fallback(q, k, v))
         else:
             res = _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated,
-                             reference, cache, out, None if dense else stats, stream)
+                             reference, cache, out, None if dense else stats, stream,
+                             "bf16" if dense else qk)
     except VedaUnsupported as e:
         if fallback is None:
             raise
@@ -422,9 +463,13 @@ def _into(out, res):
 
 
 def _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, reference,
-               cache, out, stats, stream):
+               cache, out, stats, stream, qk="bf16"):
     import torch
     S, H, D = q.shape
+    if qk not in ("bf16", "int8"):
+        raise VedaError(f"qk must be 'bf16' or 'int8', not {qk!r}")
+    if qk == "int8" and q.dtype != torch.bfloat16:
+        raise VedaUnsupported("int8 q.k products take bf16 q, k, v")
     gen, ref = budget(generated), budget(reference)
     tile_refs = not _keeps_all(ref)
     cache = {} if cache is None else cache
@@ -432,6 +477,7 @@ def _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, re
         out = torch.empty_like(q)
     # host side of every group first: layouts, budgets, buffers, attend limits
     groups = []
+    ws_bytes = 0
     for shape, heads in _head_groups(head_shapes):
         spans = [(s, g, None) for s, g in refs] if tile_refs else []
         spans.append((target[0], target[1], shape))
@@ -447,7 +493,10 @@ def _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, re
         ro = torch.empty(p.info.n_tiles + 1, dtype=torch.int32, device=q.device)
         cols = torch.empty(len(heads) * sel.entries_per_head, dtype=torch.int32, device=q.device)
         veda_attend_check(p.info, sel, p.perm, p.valid_count, q, k, v, heads, ro, cols, out)
+        if qk == "int8":
+            ws_bytes = max(ws_bytes, veda_attend_int8_query(p.info, sel))
         groups.append((key, p, heads, sel, ro, cols))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if qk == "int8" else None
     for key, p, heads, sel, ro, cols in groups:
         if not getattr(p, "built", True):
             veda_plan(p.info, p.perm, p.valid_count, stream=stream)
@@ -458,8 +507,12 @@ def _attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, re
         pk = proj_k.index_select(0, idx).contiguous()
         veda_select(p.info, sel, p.perm, p.valid_count, q, k, heads, pq, pk, row_offsets=ro,
                     cols=cols, stream=stream)
-        veda_attend(p.info, sel, p.perm, p.valid_count, q, k, v, heads, ro, cols, out=out,
-                    stream=stream)
+        if qk == "int8":
+            veda_attend_int8(p.info, sel, p.perm, p.valid_count, q, k, v, heads, ro, cols,
+                             out=out, workspace=ws, stream=stream)
+        else:
+            veda_attend(p.info, sel, p.perm, p.valid_count, q, k, v, heads, ro, cols, out=out,
+                        stream=stream)
         if stats is not None:
             stats["entries"] = stats.get("entries", 0) + len(heads) * sel.entries_per_head
             # full attention: (S / 128)^2 tile pairs per head (page `veda_core.py`,

@@ -24,7 +24,8 @@ F32, BF16 = 0, 1
 
 EXPORTS = ("veda_last_error", "veda_version", "veda_plan_query", "veda_plan",
            "veda_select_query", "veda_select", "veda_attend", "veda_attend_check",
-           "veda_select_static", "veda_teacher", "veda_recall")
+           "veda_select_static", "veda_teacher", "veda_recall", "veda_attend_int8_query",
+           "veda_attend_int8")
 
 
 class Span(C.Structure):
@@ -110,6 +111,11 @@ def load():
         "veda_attend_check": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P,
                                         P, P, C.c_int, I64, I64, I64, I64, I32, C.POINTER(I32),
                                         P, P]),
+        "veda_attend_int8_query": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo),
+                                             C.POINTER(SZ)]),
+        "veda_attend_int8": (C.c_int, [C.POINTER(PlanInfo), C.POINTER(SelectInfo), P, P, P, P, P,
+                                       P, I64, I64, I64, I64, I32, C.POINTER(I32), P, P, F, P, SZ,
+                                       P]),
     }
     for name, (res, args) in protos.items():
         if hasattr(lib, name):

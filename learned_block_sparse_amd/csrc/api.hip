@@ -5,6 +5,7 @@
 #include <cstring>
 #include <string>
 
+#include "attend_i8.hpp"
 #include "host.hpp"
 #include "kernels.hpp"
 #include "select_call.hpp"
@@ -214,6 +215,44 @@ veda_status veda_attend(const veda_plan_info *info, const veda_select_info *sel,
   hipError_t e = dtype == VEDA_BF16 ? launch_attend_bf16(a, hl, D, stream)
                                     : launch_attend_f32(a, hl, D, stream);
   return device_status(e, "attend launch");
+}
+
+veda_status veda_attend_int8(const veda_plan_info *info, const veda_select_info *sel,
+                             const int32_t *perm, const int32_t *valid_count, const void *q,
+                             const void *k, const void *v, void *out, int64_t stride_s,
+                             int64_t stride_h, int64_t out_stride_s, int64_t out_stride_h,
+                             int32_t n_heads_total, const int32_t *heads,
+                             const int32_t *row_offsets, const int32_t *cols, float scale,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  AttendArgs a;
+  HeadList hl;
+  veda_status st =
+      attend_prepare(info, sel, perm, valid_count, q, k, v, out, VEDA_BF16, stride_s, stride_h,
+                     out_stride_s, out_stride_h, n_heads_total, heads, row_offsets, cols, scale,
+                     &a, &hl);
+  if (st != VEDA_OK) return st;
+  Int8Workspace w;
+  if ((st = int8_workspace(info, sel, &w)) != VEDA_OK) return st;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(VEDA_ERR_INVALID, "workspace is NULL or not 16-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(VEDA_ERR_INVALID, "workspace smaller than veda_attend_int8_query's size");
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  QuantKArgs qa;
+  qa.k = k;
+  qa.stride_s = stride_s;
+  qa.stride_h = stride_h;
+  qa.perm = perm;
+  qa.valid_count = valid_count;
+  qa.kq = reinterpret_cast<signed char *>(ws + w.codes_off);
+  qa.kscale = reinterpret_cast<float *>(ws + w.scale_off);
+  qa.n_heads = sel->n_heads;
+  qa.n_tiles = info->n_tiles;
+  qa.head_dim = sel->head_dim;
+  hipError_t e = launch_quant_k(qa, hl, stream);
+  if (e != hipSuccess) return device_status(e, "int8 K quantisation launch");
+  e = launch_attend_i8(a, hl, sel->head_dim, qa.kq, qa.kscale, stream);
+  return device_status(e, "int8 attend launch");
 }
 
 }  // extern "C"

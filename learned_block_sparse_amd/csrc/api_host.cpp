@@ -41,4 +41,15 @@ veda_status veda_attend_check(const veda_plan_info *info, const veda_select_info
   return st;
 }
 
+veda_status veda_attend_int8_query(const veda_plan_info *info, const veda_select_info *sel,
+                                   size_t *workspace_bytes) {
+  if (!workspace_bytes) return fail(VEDA_ERR_INVALID, "workspace_bytes is NULL");
+  Int8Workspace w;
+  const veda_status st = int8_workspace(info, sel, &w);
+  if (st != VEDA_OK) return st;
+  *workspace_bytes = w.total;
+  clear_error();
+  return VEDA_OK;
+}
+
 }  // extern "C"

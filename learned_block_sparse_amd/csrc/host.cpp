@@ -362,4 +362,24 @@ veda_status attend_prepare(const veda_plan_info *info, const veda_select_info *s
   return VEDA_OK;
 }
 
+veda_status int8_workspace(const veda_plan_info *info, const veda_select_info *sel,
+                           Int8Workspace *w) {
+  veda_status st = check_info(info);
+  if (st != VEDA_OK) return st;
+  if (!sel || sel->n_blocks <= 0)
+    return fail(VEDA_ERR_INVALID, "select info is empty (call veda_select_query)");
+  if (sel->head_dim != 64 && sel->head_dim != 128)
+    return fail(VEDA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const int64_t per_head = int64_t(info->n_tiles) * VEDA_TILE * sel->head_dim;
+  if (per_head >= (int64_t(1) << 31))
+    return fail(VEDA_ERR_UNSUPPORTED, "one head's int8 K codes reach 2 GiB");
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  w->codes_off = 0;
+  w->codes_bytes = size_t(per_head) * size_t(sel->n_heads);
+  w->scale_off = up(w->codes_bytes);
+  w->scale_bytes = sizeof(float) * size_t(info->n_tiles) * size_t(sel->n_heads);
+  w->total = up(w->scale_off + w->scale_bytes);
+  return VEDA_OK;
+}
+
 }  // namespace veda

@@ -72,4 +72,16 @@ veda_status attend_prepare(const veda_plan_info *info, const veda_select_info *s
                            const int32_t *row_offsets, const int32_t *cols, float scale,
                            AttendArgs *a, HeadList *hl);
 
+// Workspace of veda_attend_int8: the int8 codes of K in tile order, then the
+// per-tile scales (byte offsets; 256-byte aligned).
+struct Int8Workspace {
+  size_t codes_off, codes_bytes;   // int8 [n_heads][n_tiles][128][D]
+  size_t scale_off, scale_bytes;   // float [n_heads][n_tiles]
+  size_t total;
+};
+// Sizes it for sel->n_heads heads of width sel->head_dim; UNSUPPORTED when
+// one head's codes reach 2^31 bytes (they are addressed with 32-bit offsets).
+veda_status int8_workspace(const veda_plan_info *info, const veda_select_info *sel,
+                           Int8Workspace *w);
+
 }  // namespace veda

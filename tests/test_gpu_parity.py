@@ -7,7 +7,12 @@ Acceptance, per the method's definition on the page `veda_core.py`:
      GPU's logits gives the GPU's lists;
   3. end to end from q/k: tile lists bit-exact (near-tie rows reported);
   4. attention under the same lists: bf16 max-abs <= 1e-2 and mean-abs <=
-     1e-3 against the fp64 oracle; float32 max-abs <= 1e-5.
+     1e-3 against the fp64 oracle; float32 max-abs <= 1e-5;
+  5. attention with int8 q.k products (veda_attend_int8): the int8 codes and
+     scales of K bit-exact against the oracle's quantiser (oracle/int8.py);
+     the output within the bf16 bounds above of the oracle's int8 attention
+     (same codes, fp64 after them) and within max-abs 5e-2 / mean-abs 2.5e-3
+     of exact attention.
 Full-size workloads compare attention on a seeded sample of query tiles
 (always including the global tiles and a ragged tile) that the oracle can
 compute one by one.
@@ -19,7 +24,7 @@ import pytest
 
 import workloads
 from edge_cases import EDGE
-from oracle import attention, budget, layer, predictor, selection, tiles
+from oracle import attention, budget, int8, layer, predictor, selection, tiles
 from gpu_common import (GpuGroup, excess_over_bf16_rounding, log, near_tie_rows, oracle_csr,
                         to_device)
 
@@ -29,6 +34,9 @@ import learned_block_sparse_amd as veda  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 BF16_MAX, BF16_MEAN, F32_MAX = 1e-2, 1e-3, 1e-5
+# int8 q.k products against exact attention: the int8 reading's own error
+# on the synthetic workloads (CPU model: max 1.9e-2, mean 1.0e-3) with room
+INT8_EXACT_MAX, INT8_EXACT_MEAN = 5e-2, 2.5e-3
 
 def _make(name):
     wl = EDGE.get(name) or workloads.get(name)
@@ -450,3 +458,125 @@ def test_teacher_map_and_recall(name):
         nv = lay.n_video
         if nv < lay.n_tiles and qt is None:
             assert np.allclose(r_got[:, nv:], 1.0, atol=1e-5)   # global rows keep every tile
+
+
+# ------------------------------------------------------- int8 q.k products --
+def _int8_workspace_views(ws, info, sel):
+    """(codes int8 [n_heads, n_tiles, 128, D], scales fp32 [n_heads, n_tiles])
+    read back from a veda_attend_int8 workspace (layout in include/veda.h)."""
+    nh, n, D = sel.n_heads, info.n_tiles, sel.head_dim
+    raw = ws.cpu().numpy()
+    nbytes = nh * n * 128 * D
+    codes = raw[:nbytes].view(np.int8).reshape(nh, n, 128, D)
+    off = (nbytes + 255) // 256 * 256
+    scales = raw[off:off + 4 * nh * n].view(np.float32).reshape(nh, n)
+    return codes, scales
+
+
+def _run_int8(gg, dev, out):
+    need = veda.veda_attend_int8_query(gg.info, gg.sel)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev["q"].device)
+    veda.veda_attend_int8(gg.info, gg.sel, gg.perm, gg.vc, dev["q"], dev["k"], dev["v"],
+                          gg.heads, gg.row_offsets, gg.cols, out=out, workspace=ws)
+    return ws
+
+
+def test_int8_codes_and_attend(case):
+    name, inp, dev, groups = case
+    if inp.workload.dtype != "bf16":
+        pytest.skip("int8 q.k products take bf16 inputs")
+    out = torch.full_like(dev["q"], float("nan"))
+    n = {"mid": 12, "headline": 6, "headline_iid": 6, "long": 4}.get(name, 10 ** 9)
+    for g in groups:
+        gg = GpuGroup(inp, dev, g.shape, g.heads, scores_mode=2, oracle_scores=g.scores)
+        log(f"[int8] {name} shape={g.shape} launching")
+        ws = _run_int8(gg, dev, out)
+        torch.cuda.synchronize()
+        codes, scales = _int8_workspace_views(ws, gg.info, gg.sel)
+        lay = g.layout
+        key_tiles = np.arange(lay.n_tiles) if lay.n_tiles <= 64 else \
+            np.unique(np.append(workloads.sample_tiles(lay.n_tiles, 40, seed=5), lay.n_tiles - 1))
+        for hi, h in enumerate(g.heads):
+            for j in key_tiles:
+                want_c, want_s = int8.key_tile_codes(inp.k, lay, h, j)
+                assert np.array_equal(codes[hi, j], want_c), (name, h, j)
+                assert scales[hi, j] == want_s, (name, h, j)
+        log(f"[int8] {name} codes of {len(key_tiles)} tiles x {len(g.heads)} heads bit-exact")
+    out_np = out.float().cpu().numpy()
+    assert np.isfinite(out_np).all(), "some rows were never written"
+    for g in groups:
+        ts = _sample_tiles(g.layout, n, seed=9 + len(g.heads))
+        rows = np.concatenate([g.layout.tile_rows(a) for a in ts])
+        got = out_np[rows][:, g.heads, :].astype(np.float64)
+        want8 = int8.attend(inp.q, inp.k, inp.v, g.layout, g.mask, g.heads, query_tiles=ts)[rows]
+        exact = attention.attend(inp.q, inp.k, inp.v, g.layout, g.mask, g.heads,
+                                 query_tiles=ts)[rows]
+        e8, ex = np.abs(got - want8), np.abs(got - exact)
+        log(f"[int8] {name} shape={g.shape} rows={len(rows)} vs int8 oracle max={e8.max():.3e} "
+            f"mean={e8.mean():.3e}; vs exact max={ex.max():.3e} mean={ex.mean():.3e}")
+        assert e8.max() <= BF16_MAX and e8.mean() <= BF16_MEAN
+        assert ex.max() <= INT8_EXACT_MAX and ex.mean() <= INT8_EXACT_MEAN
+
+
+@pytest.mark.parametrize("kind", ["late", "one_key", "early"])
+def test_int8_large_score_jumps(kind):
+    """The reference-value raise of the int8 kernel (per-tile logit factors):
+    keys scaled so later tiles jump far above the first, against the int8
+    oracle, with the bound applied beyond the output's own bf16 rounding."""
+    inp = _scaled_keys(kind)
+    dev = to_device(inp)
+    groups, _ = layer.run(inp, do_attend=False)
+    out = torch.full_like(dev["q"], float("nan"))
+    for g in groups:
+        gg = GpuGroup(inp, dev, g.shape, g.heads, scores_mode=2, oracle_scores=g.scores)
+        _run_int8(gg, dev, out)
+    torch.cuda.synchronize()
+    out_np = out.float().cpu().numpy()
+    assert np.isfinite(out_np).all()
+    for g in groups:
+        want = int8.attend(inp.q, inp.k, inp.v, g.layout, g.mask, g.heads)
+        got = out_np[:, g.heads, :].astype(np.float64)
+        err = excess_over_bf16_rounding(got, want)
+        log(f"[int8] jumps_{kind} beyond rounding max={err.max():.3e} mean={err.mean():.3e}")
+        assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+@pytest.mark.parametrize("sub", [[2], [0, 2, 3]])
+def test_int8_odd_head_subsets(sub):
+    """Odd head counts (the last pair's second group repeats a head and writes
+    nothing) leave the other heads untouched and match the int8 oracle."""
+    inp, dev, groups = _make("padding")
+    g = groups[0]
+    out = torch.full_like(dev["q"], 7.0)
+    rest = [h for h in range(inp.q.shape[1]) if h not in sub]
+    gg = GpuGroup(inp, dev, g.shape, sub)
+    _run_int8(gg, dev, out)
+    o = out.float().cpu().numpy()
+    assert (o[:, rest] == 7.0).all()
+    kept = selection.select(predictor.logits(
+        predictor.pool(inp.q, g.layout, sub), predictor.pool(inp.k, g.layout, sub),
+        inp.proj_q[sub], inp.proj_k[sub]), g.layout, g.blocks)
+    mask = selection.block_mask(kept, g.layout)
+    err = np.abs(o[:, sub] - int8.attend(inp.q, inp.k, inp.v, g.layout, mask, sub))
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+@pytest.mark.parametrize("name", ["ragged_refs", "padding"])
+def test_int8_layer_attention(name):
+    """attention(qk="int8"): head groups by box, one workspace for all, the
+    same output twice in a row (bitwise), and the int8 oracle's layer."""
+    inp, dev, groups = _make(name)
+    wl = inp.workload
+    outs = []
+    for _ in range(2):
+        outs.append(veda.attention(dev["q"], dev["k"], dev["v"], wl.refs, wl.target,
+                                   wl.head_shapes, dev["proj_q"], dev["proj_k"], wl.generated,
+                                   wl.reference, qk="int8"))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    got = outs[0].float().cpu().numpy().astype(np.float64)
+    for g in groups:
+        want = int8.attend(inp.q, inp.k, inp.v, g.layout, g.mask, g.heads)
+        rows = np.concatenate([g.layout.tile_rows(a) for a in range(g.layout.n_tiles)])
+        err = np.abs(got[rows][:, g.heads] - want[rows])
+        assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (g.shape, err.max())

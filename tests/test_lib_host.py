@@ -19,13 +19,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 HOST_ONLY_EXPORTS = {"veda_last_error", "veda_version", "veda_plan_query", "veda_select_query",
-                     "veda_attend_check"}
+                     "veda_attend_check", "veda_attend_int8_query"}
 
 
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     header = open(os.path.join(ROOT, "include", "veda.h")).read()
-    declared = set(re.findall(r"\b(veda_[a-z_]+)\s*\(", header))
+    declared = set(re.findall(r"\b(veda_[a-z_0-9]+)\s*\(", header))
     assert declared == set(_lib.EXPORTS)
     # a host-only build (the sanitizer run) carries just the host entry points
     for name in (declared if _lib.has_kernels() else HOST_ONLY_EXPORTS):
@@ -225,6 +225,50 @@ def test_attend_check_accepts_a_valid_call_and_names_bad_arguments():
     assert call(total=1) == 1 and "head index 1" in lib.veda_last_error().decode()
     assert call(ro=C.c_void_p(0)) == 1
     assert call(dtype=7) == 1
+
+
+@pytest.mark.parametrize("name,D", [("padding", 64), ("mid", 128), ("headline", 128)])
+def test_int8_workspace_size(name, D):
+    """veda_attend_int8's workspace: the int8 codes of every K tile of every
+    head (n_heads x n_tiles x 128 x D bytes), then one fp32 scale per tile
+    and head, each part rounded up to 256 bytes."""
+    wl = workloads.get(name)
+    info = veda.veda_plan_query(_spans(wl, wl.head_shapes[0]), wl.seq_len)
+    for nh in (1, 3, 24):
+        sel = veda.veda_select_query(info, veda.budget(wl.generated), veda.budget(wl.reference),
+                                     D, nh)
+        up = lambda x: -(-x // 256) * 256  # noqa: E731
+        want = up(up(nh * info.n_tiles * 128 * D) + 4 * nh * info.n_tiles)
+        assert veda.veda_attend_int8_query(info, sel) == want
+
+
+def test_int8_refuses_bad_workspace():
+    """Too small, NULL or misaligned workspaces are refused on the host before
+    anything launches; a head whose codes would reach 2 GiB is unsupported.
+    Dummy pointers, never dereferenced: the launching entry point is called
+    only where no GPU is visible."""
+    import ctypes as C
+    info = veda.veda_plan_query([(0, (4, 16, 16), None)], 1024)
+    sel = veda.veda_select_query(info, veda.budget(("tiles", 2.0)), veda.budget(("tiles", 2.0)),
+                                 64, 2)
+    need = veda.veda_attend_int8_query(info, sel)
+    big = veda.veda_plan_query([(0, (2048, 64, 128), (1, 8, 16))], 2048 * 64 * 128)
+    big_sel = veda.veda_select_query(big, veda.budget(("tiles", 1.0)), veda.budget(("tiles", 1.0)),
+                                     128, 1)
+    with pytest.raises(veda.VedaUnsupported):
+        veda.veda_attend_int8_query(big, big_sel)
+    if _gpu_visible() or not _lib.has_kernels():
+        pytest.skip("calls veda_attend_int8 with dummy pointers: CPU-only check with kernels")
+    lib = _lib.load()
+    heads = (C.c_int32 * 2)(0, 1)
+    p = C.c_void_p(1 << 20)
+
+    def call(ws=p, nbytes=need):
+        return lib.veda_attend_int8(C.byref(info), C.byref(sel), p, p, p, p, p, p, 128, 64, 128,
+                                    64, 2, heads, p, p, 0.0, ws, nbytes, None)
+    assert call(nbytes=need - 1) == 1 and "workspace smaller" in lib.veda_last_error().decode()
+    assert call(ws=C.c_void_p(0)) == 1
+    assert call(ws=C.c_void_p((1 << 20) + 8)) == 1 and "aligned" in lib.veda_last_error().decode()
 
 
 def test_index_lists_and_policy():
