@@ -58,9 +58,10 @@ def _args():
 
 
 # HBM traffic of the attend kernel, from rocprofv3 counter runs recorded in
-# this file (see it for the commands and the copy-kernel calibration). It is
+# these files (see them for the commands and the copy-kernel calibration). It is
 # reported only while the kernel source is the one the counters were taken on.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_headline_traffic.md")
+TRAFFIC_FILES = {qk: os.path.join(ROOT, "profiles", f"attend_{name}_headline_traffic.md")
+                 for qk, name in (("bf16", "bf16"), ("int8", "i8"))}
 _CSRC = os.path.join(ROOT, "learned_block_sparse_amd", "csrc")
 KERNEL_SOURCES = {
     "bf16": ("attend.hip", "attend_common.hpp", "kernels.hpp"),
@@ -84,7 +85,7 @@ def _recorded_traffic(workload, qk="bf16"):
     source."""
     import re
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[qk]) as f:
             text = f.read()
     except OSError:
         return None

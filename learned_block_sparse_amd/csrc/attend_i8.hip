@@ -341,6 +341,9 @@ __device__ __attribute__((always_inline)) inline void attend_i8_group(
       pb[kb][h][i % 8] = static_cast<__bf16>(p);
     }
   };
+  // Probabilities are formed in chunks of 8 per lane, chunk e holding block
+  // e / 2, half e % 2: A forms chunks 0 .. A_CHUNKS-1, B the rest.
+  constexpr int A_CHUNKS = 2;
   // Reference value m_run: as in the bf16 kernel, the first tile's row max,
   // raised only when a later tile's row max passes it by more than RAISE.
   constexpr float RAISE = 20.0f;
@@ -435,14 +438,12 @@ __device__ __attribute__((always_inline)) inline void attend_i8_group(
       exps8(0, c);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int e = 2; e < A_CHUNKS; ++e) exps8(e / 2, e % 2);
     barrier_lds();
     // ---- B
-    exps8(1, 0);
-    exps8(1, 1);
-    exps8(2, 0);
-    exps8(2, 1);
-    exps8(3, 0);
-    exps8(3, 1);
+#pragma unroll
+    for (int e = A_CHUNKS; e < 8; ++e) exps8(e / 2, e % 2);
     barrier_vm<C::NK>();   // V(t) landed in every wave (K(t+1) may not)
     const Rows Rv = rows_of(j1);
     __builtin_amdgcn_s_setprio(1);   // MFMA half-phases issue first
