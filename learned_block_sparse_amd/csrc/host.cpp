@@ -75,7 +75,7 @@ veda_status plan_query(const veda_span *spans, int32_t n_spans, int64_t seq_len,
                        veda_plan_info *info) {
   if (!info) return fail(VEDA_ERR_INVALID, "veda_plan_query: info is NULL");
   std::memset(info, 0, sizeof(*info));
-  if (n_spans <= 0 || !spans) return fail(VEDA_ERR_INVALID, "no video span given: the generated video must be tiled");
+  if (n_spans <= 0 || !spans) return fail(VEDA_ERR_INVALID, "no video span given: at least one span, the generated video, is required");
   if (n_spans > VEDA_MAX_SPANS)
     return fail(VEDA_ERR_INVALID, "more than " + std::to_string(VEDA_MAX_SPANS) + " spans");
   if (seq_len <= 0 || seq_len > INT32_MAX)

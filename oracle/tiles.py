@@ -130,7 +130,7 @@ def _check_spans(spans, seq_len):
     inside [0, seq_len). Reading: a negative start is refused as well (the
     page tests only order, overlap and overrun)."""
     if len(spans) == 0:
-        raise VedaError("no video span given: the generated video must be tiled")
+        raise VedaError("no video span given: at least one span, the generated video, is required")
     prev_end = 0
     for start, grid, _ in spans:
         end = start + grid[0] * grid[1] * grid[2]
