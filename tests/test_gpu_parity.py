@@ -580,3 +580,64 @@ def test_int8_layer_attention(name):
         rows = np.concatenate([g.layout.tile_rows(a) for a in range(g.layout.n_tiles)])
         err = np.abs(got[rows][:, g.heads] - want[rows])
         assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (g.shape, err.max())
+
+
+def test_int8_strided_views_and_empty_row():
+    """veda_attend_int8 on q, k, v as views into one packed [S, 3, H, D]
+    tensor equals the contiguous call bit for bit; a CSR row with no tiles
+    (the last, a global tile) writes zeros for its rows and leaves every
+    other row as with the full lists."""
+    inp, dev, groups = _make("ragged_refs")
+    packed = torch.stack([dev["q"], dev["k"], dev["v"]], dim=1).contiguous()
+    sdev = dict(dev, q=packed[:, 0], k=packed[:, 1], v=packed[:, 2])
+    for g in groups:
+        gg = GpuGroup(inp, dev, g.shape, g.heads)
+        out_a = torch.empty_like(dev["q"])
+        out_b = torch.empty_like(dev["q"])
+        _run_int8(gg, dev, out_a)
+        _run_int8(gg, sdev, out_b)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a[:, gg.heads], out_b[:, gg.heads])
+        ro = gg.row_offsets.clone()
+        ro[-1] = ro[-2]
+        out_c = veda.veda_attend_int8(gg.info, gg.sel, gg.perm, gg.vc, dev["q"], dev["k"],
+                                      dev["v"], gg.heads, ro, gg.cols)
+        torch.cuda.synchronize()
+        n = gg.info.n_tiles
+        perm = gg.perm.cpu().numpy()
+        last = perm[(n - 1) * 128:n * 128]
+        last = last[last >= 0]
+        a = out_a[:, gg.heads].float().cpu().numpy()
+        c = out_c[:, gg.heads].float().cpu().numpy()
+        assert (c[last] == 0).all()
+        keep = np.setdiff1d(np.arange(a.shape[0]), last)
+        assert np.array_equal(a[keep], c[keep])
+
+
+def test_int8_zero_tiles_and_rows():
+    """Degenerate scales: one key tile whose real rows are all zero (scale 0,
+    codes 0, its logits exactly 0) and some query rows of zeros (every
+    logit 0: the row averages its kept values). Against the int8 oracle."""
+    inp = workloads.generate("padding")
+    groups, _ = layer.run(inp, do_attend=False)
+    g = groups[0]
+    lay = g.layout
+    q, k = inp.q.copy(), inp.k.copy()
+    zero_tile = int(lay.n_video // 2)
+    k[lay.tile_rows(zero_tile)] = 0.0
+    zero_rows = lay.tile_rows(3)[:5]
+    q[zero_rows] = 0.0
+    inp = dataclasses.replace(inp, q=q, k=k)
+    dev = to_device(inp)
+    gg = GpuGroup(inp, dev, g.shape, g.heads, scores_mode=2, oracle_scores=g.scores)
+    out = torch.full_like(dev["q"], float("nan"))
+    ws = _run_int8(gg, dev, out)
+    torch.cuda.synchronize()
+    codes, scales = _int8_workspace_views(ws, gg.info, gg.sel)
+    assert (scales[:, zero_tile] == 0).all() and not codes[:, zero_tile].any()
+    got = out.float().cpu().numpy().astype(np.float64)[:, g.heads]
+    assert np.isfinite(got).all()
+    want = int8.attend(inp.q, inp.k, inp.v, lay, g.mask, g.heads)
+    err = np.abs(got - want)
+    log(f"[int8] zero tile/rows max={err.max():.3e} mean={err.mean():.3e}")
+    assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
