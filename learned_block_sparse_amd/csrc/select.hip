@@ -243,8 +243,11 @@ struct RowKeys {
   __device__ uint64_t get(int j) const { return lds ? lds[j] : compute(j); }
 };
 
-__global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
-  __shared__ uint64_t keys_lds[SEL_WAVES][SEL_LDS_KEYS];
+// The keys of a wave's row sit in dynamic LDS sized to the widest selecting
+// block of the call (at most SEL_LDS_KEYS per wave; a wider block recomputes
+// its keys on every pass), so narrow layouts fit more workgroups per CU.
+__global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, int32_t stash_keys) {
+  extern __shared__ uint64_t keys_dyn[];
   __shared__ int32_t hist_lds[SEL_WAVES][256];
   const int wave = threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
@@ -273,7 +276,7 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
     emit_all(0, a.n_tiles);
     return;
   }
-  uint64_t *stash = keys_lds[wave];
+  uint64_t *stash = keys_dyn + int64_t(wave) * stash_keys;
   int32_t *hist = hist_lds[wave];
   for (int b = 0; b < a.n_blocks; ++b) {
     const veda_block blk = a.blocks[b];
@@ -290,7 +293,7 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
     rk.start = blk.start;
     rk.own = (r >= blk.start && r < blk.stop) ? int32_t(r - blk.start) : -1;
     rk.lds = nullptr;
-    if (n <= SEL_LDS_KEYS) {
+    if (n <= stash_keys) {
       for (int j = lane; j < n; j += 64) stash[j] = rk.compute(j);
       rk.lds = stash;
       wave_sync();
@@ -365,7 +368,12 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   dim3 grid((a.n_tiles + SEL_WAVES - 1) / SEL_WAVES, a.n_heads);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(64 * SEL_WAVES), 0, s, a);
+  int32_t widest = 0;
+  for (int b = 0; b < a.n_blocks; ++b)
+    if (!a.blocks[b].keep_all) widest = max(widest, a.blocks[b].stop - a.blocks[b].start);
+  const int32_t stash = min(widest, SEL_LDS_KEYS);
+  const size_t lds = size_t(SEL_WAVES) * size_t(stash) * sizeof(uint64_t);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(64 * SEL_WAVES), lds, s, a, stash);
   return hipGetLastError();
 }
 
