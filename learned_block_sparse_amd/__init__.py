@@ -261,6 +261,8 @@ def veda_attend_int8(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, v
     need = veda_attend_int8_query(info, sel)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise VedaError("workspace must be a contiguous device tensor")
     _check(_lib.load().veda_attend_int8(
         C.byref(info), C.byref(sel), _ptr(perm), _ptr(valid_count), _ptr(q), _ptr(k), _ptr(v),
         _ptr(out), q.stride(0), q.stride(1), out.stride(0), out.stride(1), q.shape[1], harr,
