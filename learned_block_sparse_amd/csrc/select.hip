@@ -19,70 +19,111 @@
 namespace veda {
 
 // ------------------------------------------------------------------ pool --
+// One wave per (video tile, q or k, head): 16-byte row reads, LPR lanes per
+// head row, so one load instruction covers RPL rows and the wave keeps all of
+// the tile's rows in flight. Each lane folds its rows into fp64 sums (exact
+// for bf16 and f32 inputs of a tile's range, so the order does not matter)
+// and fp32 max / min; the RPL lane groups are then combined by lane
+// exchanges, and the first group writes the features.
+template <int D, bool BF16>
 __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a, HeadList heads,
                                                    const int32_t *__restrict__ perm,
                                                    const int32_t *__restrict__ valid_count) {
+  constexpr int VPL = BF16 ? 8 : 4;        // values per 16-byte read
+  constexpr int LPR = D / VPL;             // lanes per head row
+  constexpr int RPL = 64 / LPR;            // rows per load instruction
   __shared__ int32_t rows[VEDA_TILE];
   const int32_t tile = blockIdx.x;
   const int which = blockIdx.y;  // 0: q, 1: k
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int hi = blockIdx.z * 4 + wave;
   const int32_t count = valid_count[tile];
   if (threadIdx.x < VEDA_TILE) rows[threadIdx.x] = perm[int64_t(tile) * VEDA_TILE + threadIdx.x];
   __syncthreads();
-  const int D = a.head_dim;
-  const int half = D / 2;
-  const int n_pairs = a.n_heads * half;
-  for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
-    const int hi = p / half;
-    const int c = (p % half) * 2;
-    const int64_t col = int64_t(heads.h[hi]) * a.stride_h + c;
-    double s0 = 0.0, s1 = 0.0;
-    float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY;
-    if (a.is_bf16) {
-      const uint16_t *x = static_cast<const uint16_t *>(a.x[which]);
-      for (int i = 0; i < count; ++i) {
-        const uint32_t u = *reinterpret_cast<const uint32_t *>(x + int64_t(rows[i]) * a.stride_s + col);
-        const float v0 = __uint_as_float(u << 16), v1 = __uint_as_float(u & 0xffff0000u);
-        s0 += double(v0);
-        s1 += double(v1);
-        mx0 = fmaxf(mx0, v0); mx1 = fmaxf(mx1, v1);
-        mn0 = fminf(mn0, v0); mn1 = fminf(mn1, v1);
+  if (hi >= a.n_heads) return;
+  const int c = (lane % LPR) * VPL;
+  const int rsub = lane / LPR;
+  const unsigned char *base = static_cast<const unsigned char *>(a.x[which]) +
+                              (int64_t(heads.h[hi]) * a.stride_h + c) * (BF16 ? 2 : 4);
+  const int64_t pitch = a.stride_s * (BF16 ? 2 : 4);
+  double sum[VPL];
+  float mx[VPL], mn[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    sum[v] = 0.0;
+    mx[v] = -INFINITY;
+    mn[v] = INFINITY;
+  }
+#pragma unroll 8
+  for (int r = rsub; r < count; r += RPL) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(base + int64_t(rows[r]) * pitch);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float x[VPL];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
       }
     } else {
-      const float *x = static_cast<const float *>(a.x[which]);
-      for (int i = 0; i < count; ++i) {
-        const float2 v = *reinterpret_cast<const float2 *>(x + int64_t(rows[i]) * a.stride_s + col);
-        s0 += double(v.x);
-        s1 += double(v.y);
-        mx0 = fmaxf(mx0, v.x); mx1 = fmaxf(mx1, v.y);
-        mn0 = fminf(mn0, v.x); mn1 = fminf(mn1, v.y);
-      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
     }
-    double *f = a.feat + ((int64_t(which) * a.n_heads + hi) * a.n_video + tile) * (3 * D);
-    if (count > 0) {
-      f[c] = s0 / double(count);
-      f[c + 1] = s1 / double(count);
-      f[D + c] = double(mx0);
-      f[D + c + 1] = double(mx1);
-      f[2 * D + c] = double(mn0);
-      f[2 * D + c + 1] = double(mn1);
-    } else {
-      f[c] = f[c + 1] = f[D + c] = f[D + c + 1] = f[2 * D + c] = f[2 * D + c + 1] = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      sum[v] += double(x[v]);
+      mx[v] = fmaxf(mx[v], x[v]);
+      mn[v] = fminf(mn[v], x[v]);
     }
+  }
+#pragma unroll
+  for (int m = LPR; m < 64; m *= 2) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      sum[v] += __shfl_xor(sum[v], m, 64);
+      mx[v] = fmaxf(mx[v], __shfl_xor(mx[v], m, 64));
+      mn[v] = fminf(mn[v], __shfl_xor(mn[v], m, 64));
+    }
+  }
+  if (rsub != 0) return;
+  double *f = a.feat + ((int64_t(which) * a.n_heads + hi) * a.n_video + tile) * (3 * D);
+  const double n_rows = count > 0 ? double(count) : 1.0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    f[c + v] = count > 0 ? sum[v] / n_rows : 0.0;
+    f[D + c + v] = count > 0 ? double(mx[v]) : 0.0;
+    f[2 * D + c + v] = count > 0 ? double(mn[v]) : 0.0;
   }
 }
 
 hipError_t launch_pool(const PoolArgs &a, const HeadList &heads, const int32_t *perm,
                        const int32_t *valid_count, hipStream_t s) {
-  hipLaunchKernelGGL(pool_kernel, dim3(a.n_video, 2), dim3(256), 0, s, a, heads, perm,
-                     valid_count);
+  const dim3 grid(a.n_video, 2, (a.n_heads + 3) / 4);
+  if (a.head_dim == 128) {
+    if (a.is_bf16)
+      hipLaunchKernelGGL((pool_kernel<128, true>), grid, dim3(256), 0, s, a, heads, perm, valid_count);
+    else
+      hipLaunchKernelGGL((pool_kernel<128, false>), grid, dim3(256), 0, s, a, heads, perm, valid_count);
+  } else {
+    if (a.is_bf16)
+      hipLaunchKernelGGL((pool_kernel<64, true>), grid, dim3(256), 0, s, a, heads, perm, valid_count);
+    else
+      hipLaunchKernelGGL((pool_kernel<64, false>), grid, dim3(256), 0, s, a, heads, perm, valid_count);
+  }
   return hipGetLastError();
 }
 
 // --------------------------------------------------------------- project --
 // fp64 GEMM C = A B for the two small products of the predictor (about 4 and
-// 5 GFLOP at the headline): a 64 x 64 output tile per 256-thread block, K in
-// steps of 16 staged in LDS k-major, each thread a 4 x 4 register tile whose
-// four A and four B values are contiguous (two 16-byte LDS reads each).
+// 5 GFLOP at 870 video tiles): a 64 x 64 output tile per 256-thread block, K
+// in steps of 16 staged in LDS k-major, each thread a 4 x 4 register tile
+// whose four A and four B values are contiguous (two 16-byte LDS reads each).
+// Two schedules of the same arithmetic: gemm_tile stages one step at a time
+// (68 registers, one 17 KB buffer: seven blocks fit a CU), gemm_tile_pipelined
+// keeps the next step's global reads in flight during the current step's
+// products (two LDS buffers, four blocks per CU). The projection (K = 3D,
+// about five blocks per CU at 870 tiles) runs faster with every block
+// resident; the logits (K = D, many rounds of blocks) with the pipeline.
 constexpr int GT = 64, GK = 16;
 
 struct GemmTile {
@@ -132,6 +173,68 @@ __device__ inline void gemm_tile(const double *A, int M, int K, int i0, int j0, 
   }
 }
 
+constexpr int GPER = GT * GK / 256;   // A (and B) elements one thread stages per k step
+
+// gemm_tile for an n-major B with two LDS buffers: the global reads of step
+// s + 1 are in flight (in registers) while step s multiplies out of LDS, and
+// one barrier per step separates a buffer's reads from its next fill.
+template <class LoadB>
+__device__ inline void gemm_tile_pipelined(const double *A, int M, int K, int i0, int j0, int N,
+                                           LoadB load_b, GemmTile &t) {
+  // rows padded to 66 doubles (528 B, still 16-byte aligned): the k-fastest
+  // stores of 16 lanes then land in distinct banks
+  __shared__ __attribute__((aligned(16))) double As[2][GK][GT + 2];
+  __shared__ __attribute__((aligned(16))) double Bs[2][GK][GT + 2];
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) t.acc[u][w] = 0.0;
+  double ra[GPER], rb[GPER];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < GPER; ++e) {
+      const int idx = int(threadIdx.x) + 256 * e;
+      const int r = idx / GK, kk = idx % GK;   // GK consecutive k of one row of A and of B
+      ra[e] = (i0 + r < M && k0 + kk < K) ? A[int64_t(i0 + r) * K + k0 + kk] : 0.0;
+      rb[e] = (j0 + r < N && k0 + kk < K) ? load_b(k0 + kk, j0 + r) : 0.0;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < GPER; ++e) {
+      const int idx = int(threadIdx.x) + 256 * e;
+      const int r = idx / GK, kk = idx % GK;
+      As[buf][kk][r] = ra[e];
+      Bs[buf][kk][r] = rb[e];
+    }
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < K; k0 += GK) {
+    const bool more = k0 + GK < K;
+    if (more) fetch(k0 + GK);
+#pragma unroll 4
+    for (int kk = 0; kk < GK; ++kk) {
+      const double2 a01 = *reinterpret_cast<const double2 *>(&As[buf][kk][ty * 4]);
+      const double2 a23 = *reinterpret_cast<const double2 *>(&As[buf][kk][ty * 4 + 2]);
+      const double2 b01 = *reinterpret_cast<const double2 *>(&Bs[buf][kk][tx * 4]);
+      const double2 b23 = *reinterpret_cast<const double2 *>(&Bs[buf][kk][tx * 4 + 2]);
+      const double av[4] = {a01.x, a01.y, a23.x, a23.y};
+      const double bv[4] = {b01.x, b01.y, b23.x, b23.y};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) t.acc[u][w] = fma(av[u], bv[w], t.acc[u][w]);
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
 // Projection (page `veda_core.py`, § predictor, `logits`): x_hat = f P + mean,
 // f = [mean | max | min] (3D wide), P [3D][D] per head; the mean is the first
 // D features of f.
@@ -173,7 +276,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a) {
   const double *A = a.qh + int64_t(hi) * nv * D;
   const double *B = a.kh + int64_t(hi) * nv * D;
   GemmTile t;
-  gemm_tile<true>(A, nv, D, i0, j0, nv, [&](int k, int n) { return B[int64_t(n) * D + k]; }, t);
+  gemm_tile_pipelined(A, nv, D, i0, j0, nv, [&](int k, int n) { return B[int64_t(n) * D + k]; }, t);
   double *C = a.scores + int64_t(hi) * nv * nv;
   double *C2 = a.scores_copy ? a.scores_copy + int64_t(hi) * nv * nv : nullptr;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
