@@ -337,12 +337,12 @@ struct RowKeys {
   const int32_t *vc;
   int32_t start, own;   // own = column of the row's own tile inside the block, or -1
   uint64_t *lds;        // NULL when the block is wider than the LDS stash
-  __device__ uint64_t compute(int j) const {
-    double s = srow[start + j];
-    if (vc[start + j] <= 0) s = -INFINITY;
+  __device__ uint64_t key_of(double s, int32_t count, int j) const {
+    if (count <= 0) s = -INFINITY;
     if (j == own) s = INFINITY;
     return order_key(s);
   }
+  __device__ uint64_t compute(int j) const { return key_of(srow[start + j], vc[start + j], j); }
   __device__ uint64_t get(int j) const { return lds ? lds[j] : compute(j); }
 };
 
@@ -397,7 +397,21 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
     rk.own = (r >= blk.start && r < blk.stop) ? int32_t(r - blk.start) : -1;
     rk.lds = nullptr;
     if (n <= stash_keys) {
-      for (int j = lane; j < n; j += 64) stash[j] = rk.compute(j);
+      // eight logits per lane in flight at a time (indices past the block
+      // re-read its last column and are not stored)
+      for (int j0 = lane; j0 < n; j0 += 64 * 8) {
+        double sv[8];
+        int32_t cv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(j0 + 64 * u, n - 1);
+          sv[u] = rk.srow[rk.start + j];
+          cv[u] = rk.vc[rk.start + j];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j0 + 64 * u < n) stash[j0 + 64 * u] = rk.key_of(sv[u], cv[u], j0 + 64 * u);
+      }
       rk.lds = stash;
       wave_sync();
     }
