@@ -121,9 +121,11 @@ hipError_t launch_pool(const PoolArgs &a, const HeadList &heads, const int32_t *
 // Two schedules of the same arithmetic: gemm_tile stages one step at a time
 // (68 registers, one 17 KB buffer: seven blocks fit a CU), gemm_tile_pipelined
 // keeps the next step's global reads in flight during the current step's
-// products (two LDS buffers, four blocks per CU). The projection (K = 3D,
-// about five blocks per CU at 870 tiles) runs faster with every block
-// resident; the logits (K = D, many rounds of blocks) with the pipeline.
+// products (two LDS buffers, four blocks per CU). The logits (K = D, many
+// rounds of blocks) always run pipelined; the projection (K = 3D) only when
+// its grid fits the chip in one round of four blocks per CU, and otherwise
+// staged, so that all of its blocks stay resident (about five per CU at 870
+// video tiles).
 constexpr int GT = 64, GK = 16;
 
 struct GemmTile {
@@ -175,10 +177,10 @@ __device__ inline void gemm_tile(const double *A, int M, int K, int i0, int j0, 
 
 constexpr int GPER = GT * GK / 256;   // A (and B) elements one thread stages per k step
 
-// gemm_tile for an n-major B with two LDS buffers: the global reads of step
-// s + 1 are in flight (in registers) while step s multiplies out of LDS, and
-// one barrier per step separates a buffer's reads from its next fill.
-template <class LoadB>
+// gemm_tile with two LDS buffers: the global reads of step s + 1 are in
+// flight (in registers) while step s multiplies out of LDS, and one barrier
+// per step separates a buffer's reads from its next fill.
+template <bool B_NK, class LoadB>
 __device__ inline void gemm_tile_pipelined(const double *A, int M, int K, int i0, int j0, int N,
                                            LoadB load_b, GemmTile &t) {
   // rows padded to 66 doubles (528 B, still 16-byte aligned): the k-fastest
@@ -195,9 +197,14 @@ __device__ inline void gemm_tile_pipelined(const double *A, int M, int K, int i0
 #pragma unroll
     for (int e = 0; e < GPER; ++e) {
       const int idx = int(threadIdx.x) + 256 * e;
-      const int r = idx / GK, kk = idx % GK;   // GK consecutive k of one row of A and of B
+      const int r = idx / GK, kk = idx % GK;   // A: GK consecutive k of one row
       ra[e] = (i0 + r < M && k0 + kk < K) ? A[int64_t(i0 + r) * K + k0 + kk] : 0.0;
-      rb[e] = (j0 + r < N && k0 + kk < K) ? load_b(k0 + kk, j0 + r) : 0.0;
+      if constexpr (B_NK) {
+        rb[e] = (j0 + r < N && k0 + kk < K) ? load_b(k0 + kk, j0 + r) : 0.0;
+      } else {
+        const int kb = idx / GT, c = idx % GT;    // B: 64 consecutive n of one k
+        rb[e] = (j0 + c < N && k0 + kb < K) ? load_b(k0 + kb, j0 + c) : 0.0;
+      }
     }
   };
   auto stash = [&](int buf) {
@@ -206,7 +213,12 @@ __device__ inline void gemm_tile_pipelined(const double *A, int M, int K, int i0
       const int idx = int(threadIdx.x) + 256 * e;
       const int r = idx / GK, kk = idx % GK;
       As[buf][kk][r] = ra[e];
-      Bs[buf][kk][r] = rb[e];
+      if constexpr (B_NK) {
+        Bs[buf][kk][r] = rb[e];
+      } else {
+        const int kb = idx / GT, c = idx % GT;
+        Bs[buf][kb][c] = rb[e];
+      }
     }
   };
   fetch(0);
@@ -238,14 +250,19 @@ __device__ inline void gemm_tile_pipelined(const double *A, int M, int K, int i0
 // Projection (page `veda_core.py`, § predictor, `logits`): x_hat = f P + mean,
 // f = [mean | max | min] (3D wide), P [3D][D] per head; the mean is the first
 // D features of f.
+template <bool PIPELINED>
 __global__ void __launch_bounds__(256) project_kernel(ProjectArgs a) {
   const int D = a.head_dim, K = 3 * D, nv = a.n_video;
   const int hi = blockIdx.z >> 1, which = blockIdx.z & 1;
   const int i0 = blockIdx.y * GT, j0 = blockIdx.x * GT;
   const double *F = a.feat + (int64_t(which) * a.n_heads + hi) * nv * K;
   const float *P = a.proj[which] + int64_t(hi) * K * D;
+  auto load_p = [&](int k, int n) { return double(P[int64_t(k) * D + n]); };
   GemmTile t;
-  gemm_tile<false>(F, nv, K, i0, j0, D, [&](int k, int n) { return double(P[int64_t(k) * D + n]); }, t);
+  if constexpr (PIPELINED)
+    gemm_tile_pipelined<false>(F, nv, K, i0, j0, D, load_p, t);
+  else
+    gemm_tile<false>(F, nv, K, i0, j0, D, load_p, t);
   double *dst = a.out + (int64_t(which) * a.n_heads + hi) * nv * D;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
 #pragma unroll
@@ -260,9 +277,17 @@ __global__ void __launch_bounds__(256) project_kernel(ProjectArgs a) {
   }
 }
 
+// Grids up to this many projection blocks fit the chip in one round at the
+// pipelined schedule's four blocks per CU (256 CUs); larger ones run the
+// staged schedule, whose seven blocks per CU keep them resident.
+constexpr int64_t PROJECT_PIPELINED_MAX_BLOCKS = 1024;
+
 hipError_t launch_project(const ProjectArgs &a, hipStream_t s) {
   const dim3 grid((a.head_dim + GT - 1) / GT, (a.n_video + GT - 1) / GT, 2 * a.n_heads);
-  hipLaunchKernelGGL(project_kernel, grid, dim3(256), 0, s, a);
+  if (int64_t(grid.x) * grid.y * grid.z <= PROJECT_PIPELINED_MAX_BLOCKS)
+    hipLaunchKernelGGL(project_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(project_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -276,7 +301,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a) {
   const double *A = a.qh + int64_t(hi) * nv * D;
   const double *B = a.kh + int64_t(hi) * nv * D;
   GemmTile t;
-  gemm_tile_pipelined(A, nv, D, i0, j0, nv, [&](int k, int n) { return B[int64_t(n) * D + k]; }, t);
+  gemm_tile_pipelined<true>(A, nv, D, i0, j0, nv, [&](int k, int n) { return B[int64_t(n) * D + k]; }, t);
   double *C = a.scores + int64_t(hi) * nv * nv;
   double *C2 = a.scores_copy ? a.scores_copy + int64_t(hi) * nv * nv : nullptr;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
