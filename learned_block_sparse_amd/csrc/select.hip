@@ -368,7 +368,6 @@ struct RowKeys {
     return order_key(s);
   }
   __device__ uint64_t compute(int j) const { return key_of(srow[start + j], vc[start + j], j); }
-  __device__ uint64_t get(int j) const { return lds ? lds[j] : compute(j); }
 };
 
 // The keys of a wave's row sit in dynamic LDS sized to the widest selecting
@@ -445,9 +444,23 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
     for (int shift = 56; shift >= 0; shift -= 8) {
       for (int i = lane; i < 256; i += 64) hist[i] = 0;
       wave_sync();
-      for (int j = lane; j < n; j += 64) {
-        const uint64_t key = rk.get(j);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      if (rk.lds) {
+        // eight stashed keys per lane read at a time (indices past the block
+        // re-read its last key and are not counted)
+        for (int j0 = lane; j0 < n; j0 += 64 * 8) {
+          uint64_t kv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) kv[u] = rk.lds[min(j0 + 64 * u, n - 1)];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (j0 + 64 * u < n && (kv[u] & mask) == prefix)
+              atomicAdd(&hist[(kv[u] >> shift) & 255], 1);
+        }
+      } else {
+        for (int j = lane; j < n; j += 64) {
+          const uint64_t key = rk.compute(j);
+          if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+        }
       }
       wave_sync();
       const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
@@ -485,23 +498,33 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
       wave_sync();
       if (bucket == k) break;   // the whole bucket is kept: no finer digit needed
     }
-    // Emit: keys above the prefix, and the first k keys equal to it by column.
+    // Emit: keys above the prefix, and the first k keys equal to it by column
+    // (eight keys per lane read at a time, as in the histogram passes).
     const uint64_t neg_inf = order_key(-INFINITY);
     int eq_before = 0;
-    for (int base = 0; base < n; base += 64) {
-      const int j = base + lane;
-      const bool valid = j < n;
-      const uint64_t key = valid ? rk.get(j) : 0;
-      const uint64_t mk = key & mask;
-      const bool gt = valid && mk > prefix;
-      const bool eq = valid && mk == prefix;
-      const uint64_t eqm = __ballot(eq);
-      const int eqrank = eq_before + __popcll(eqm & lt_mask);
-      const bool keep = (gt || (eq && eqrank < k)) && key != neg_inf;
-      const uint64_t km = __ballot(keep);
-      if (keep) out[pos + __popcll(km & lt_mask)] = blk.start + j;
-      pos += __popcll(km);
-      eq_before += __popcll(eqm);
+    for (int base = 0; base < n; base += 64 * 8) {
+      uint64_t kv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(base + 64 * u + lane, n - 1);
+        kv[u] = rk.lds ? rk.lds[j] : rk.compute(j);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = base + 64 * u + lane;
+        const bool valid = j < n;
+        const uint64_t key = kv[u];
+        const uint64_t mk = key & mask;
+        const bool gt = valid && mk > prefix;
+        const bool eq = valid && mk == prefix;
+        const uint64_t eqm = __ballot(eq);
+        const int eqrank = eq_before + __popcll(eqm & lt_mask);
+        const bool keep = (gt || (eq && eqrank < k)) && key != neg_inf;
+        const uint64_t km = __ballot(keep);
+        if (keep) out[pos + __popcll(km & lt_mask)] = blk.start + j;
+        pos += __popcll(km);
+        eq_before += __popcll(eqm);
+      }
     }
     wave_sync();
   }
