@@ -28,6 +28,14 @@ EDGE = {
     # fp32 with global rows and padding
     "f32_padding": dataclasses.replace(_base, name="f32_padding", index=15,
                                        dtype="f32", head_dim=128),
+    # head_dim 64 over many tiles: locality bias, a reference span, a ragged
+    # target (w = 46), text rows before and after, and five heads in three
+    # tile boxes (a group of three heads, and two single-head groups)
+    "d64_bias": dataclasses.replace(
+        _base, name="d64_bias", index=17, seq_len=11000, n_heads=5, head_dim=64,
+        refs=((64, (1, 24, 40)),), target=(1024, (9, 24, 46)),
+        head_shapes=(None, (1, 8, 16), None, (2, 8, 8), (4, 4, 8)),
+        generated=("sparsity", 0.8), reference=("sparsity", 0.7), bias=True),
     # a reference span whose budget keeps everything: it is not tiled, its
     # rows join the text rows as global rows
     "refs_whole": dataclasses.replace(
