@@ -425,7 +425,7 @@ def test_full_attention_policy_runs_keep_all_kernels():
     assert veda.summary(stats).startswith("Attention computed: 100.0%")
 
 
-@pytest.mark.parametrize("name", ["padding", "refs_whole", "ragged_refs", "mid"])
+@pytest.mark.parametrize("name", ["padding", "refs_whole", "ragged_refs", "d64_bias", "mid"])
 def test_teacher_map_and_recall(name):
     """The max-pooled full-attention teacher map and the recall of the
     selected tile lists against the oracle (oracle/teacher.py): the map
