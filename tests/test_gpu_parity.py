@@ -220,7 +220,7 @@ def test_run_to_run_bitwise_determinism(name):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["ragged_refs", "refs_whole", "padding"])
+@pytest.mark.parametrize("name", ["ragged_refs", "refs_whole", "padding", "d64_bias"])
 def test_layer_attention_matches_oracle(name):
     """The one-call layer (head groups by tile box, references tiled, cached
     plans) against the oracle's whole layer, and its receipt."""
@@ -561,7 +561,7 @@ def test_int8_odd_head_subsets(sub):
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
 
 
-@pytest.mark.parametrize("name", ["ragged_refs", "padding"])
+@pytest.mark.parametrize("name", ["ragged_refs", "padding", "d64_bias"])
 def test_int8_layer_attention(name):
     """attention(qk="int8"): head groups by box, one workspace for all, the
     same output twice in a row (bitwise), and the int8 oracle's layer."""
