@@ -36,6 +36,15 @@ EDGE = {
         refs=((64, (1, 24, 40)),), target=(1024, (9, 24, 46)),
         head_shapes=(None, (1, 8, 16), None, (2, 8, 8), (4, 4, 8)),
         generated=("sparsity", 0.8), reference=("sparsity", 0.7), bias=True),
+    # the most heads one call takes (VEDA_MAX_HEADS)
+    "max_heads": dataclasses.replace(_base, name="max_heads", index=18, n_heads=256,
+                                     head_shapes=(None,) * 256),
+    # the most spans one plan takes (VEDA_MAX_SPANS): 15 one-tile references,
+    # each with text rows before it, then the target
+    "max_spans": dataclasses.replace(
+        _base, name="max_spans", index=19, seq_len=15 * 40 + 8 + 512 + 24, n_heads=2,
+        refs=tuple((8 + 40 * i, (1, 4, 8)) for i in range(15)), target=(608, (2, 16, 16)),
+        head_shapes=(None, None), generated=("ratio", 0.3), reference=("ratio", 0.4)),
     # a reference span whose budget keeps everything: it is not tiled, its
     # rows join the text rows as global rows
     "refs_whole": dataclasses.replace(

@@ -49,7 +49,7 @@ def _make(name):
 
 
 SMALL = ["tiny", "padding", "one_cell", "ragged_refs", "refs_whole", "keep_all", "tiles_big",
-         "f32_padding", "d64_bias"]
+         "f32_padding", "d64_bias", "max_heads", "max_spans"]
 BIG = ["mid", "headline", "headline_iid", "long"]
 
 
