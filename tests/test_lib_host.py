@@ -6,6 +6,8 @@ import math
 import os
 import random
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -331,3 +333,24 @@ def test_summary_receipt():
     lines = veda.receipt({"entries": 109, "dense": 1000.0, "sparse_calls": 160,
                           "dense_calls": 40}).splitlines()
     assert lines[0].startswith("Veda done") and lines[2] == "Calls: 160 sparse, 40 dense"
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With libveda.so absent, the first call into the package raises and
+    names the build step; nothing falls back to another compute path."""
+    code = (
+        "import learned_block_sparse_amd as veda\n"
+        "for call in (lambda: veda.veda_plan_query([(0, (4, 16, 16), None)], 1024),\n"
+        "             veda.version):\n"
+        "    try:\n"
+        "        call()\n"
+        "    except RuntimeError as e:\n"
+        "        assert 'not found' in str(e) and 'no fallback' in str(e), e\n"
+        "    else:\n"
+        "        raise SystemExit('no error')\n"
+        "print('ok')\n")
+    env = dict(os.environ, VEDA_LIBRARY=str(tmp_path / "absent" / "libveda.so"),
+               CUDA_VISIBLE_DEVICES="", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
