@@ -242,6 +242,34 @@ def test_layer_attention_matches_oracle(name):
     assert veda.summary(stats).startswith("Attention computed: ")
 
 
+def test_calls_run_on_the_callers_stream():
+    """Every stage is enqueued on the caller's current stream: on a side
+    stream that first spins (a bounded sleep kernel) and only then copies q,
+    k and v into zeroed buffers, the layer equals the default-stream result
+    bit for bit; a stage launched on another stream would read the zeros."""
+    inp, dev, groups = _make("padding")
+    wl = inp.workload
+    args = (wl.refs, wl.target, wl.head_shapes, dev["proj_q"], dev["proj_k"], wl.generated,
+            wl.reference)
+    want = veda.attention(dev["q"], dev["k"], dev["v"], *args)
+    q0, k0, v0 = (torch.zeros_like(dev[n]) for n in "qkv")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):
+        e0.record(side)
+        torch.cuda._sleep(50_000_000)
+        e1.record(side)
+        q0.copy_(dev["q"])
+        k0.copy_(dev["k"])
+        v0.copy_(dev["v"])
+        got = veda.attention(q0, k0, v0, *args)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) >= 5.0   # the window a stage on another stream would fall in
+    assert torch.equal(got, want)
+
+
 @pytest.mark.parametrize("name", ["padding", "f32_padding"])
 def test_empty_tile_list_row_leaves_zeros(name):
     """A CSR row with no tiles (veda_select never makes one; veda_attend takes
