@@ -270,6 +270,34 @@ def test_calls_run_on_the_callers_stream():
     assert torch.equal(got, want)
 
 
+def test_two_streams_at_once_do_not_interfere():
+    """Two layers in flight together on two streams (different inputs, each
+    with its own workspaces) give what each gives alone, bit for bit: the
+    library keeps no state between calls besides veda_select_static's
+    scratch, which this path does not use."""
+    inp, dev, groups = _make("ragged_refs")
+    wl = inp.workload
+    args = (wl.refs, wl.target, wl.head_shapes, dev["proj_q"], dev["proj_k"], wl.generated,
+            wl.reference)
+    other = {n: (dev[n].float().flip(0) * 0.75).to(dev[n].dtype).contiguous() for n in "qkv"}
+    want_a = veda.attention(dev["q"], dev["k"], dev["v"], *args)
+    want_b = veda.attention(other["q"], other["k"], other["v"], *args)
+    want_b8 = veda.attention(other["q"], other["k"], other["v"], *args, qk="int8")
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            got_a = veda.attention(dev["q"], dev["k"], dev["v"], *args)
+        with torch.cuda.stream(s2):
+            got_b = veda.attention(other["q"], other["k"], other["v"], *args)
+            got_b8 = veda.attention(other["q"], other["k"], other["v"], *args, qk="int8")
+        s1.synchronize()
+        s2.synchronize()
+        assert torch.equal(got_a, want_a)
+        assert torch.equal(got_b, want_b)
+        assert torch.equal(got_b8, want_b8)
+
+
 @pytest.mark.parametrize("name", ["padding", "f32_padding"])
 def test_empty_tile_list_row_leaves_zeros(name):
     """A CSR row with no tiles (veda_select never makes one; veda_attend takes
