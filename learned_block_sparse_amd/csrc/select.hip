@@ -421,19 +421,19 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
     rk.own = (r >= blk.start && r < blk.stop) ? int32_t(r - blk.start) : -1;
     rk.lds = nullptr;
     if (n <= stash_keys) {
-      // eight logits per lane in flight at a time (indices past the block
+      // sixteen logits per lane in flight at a time (indices past the block
       // re-read its last column and are not stored)
-      for (int j0 = lane; j0 < n; j0 += 64 * 8) {
-        double sv[8];
-        int32_t cv[8];
+      for (int j0 = lane; j0 < n; j0 += 64 * 16) {
+        double sv[16];
+        int32_t cv[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const int j = min(j0 + 64 * u, n - 1);
           sv[u] = rk.srow[rk.start + j];
           cv[u] = rk.vc[rk.start + j];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
           if (j0 + 64 * u < n) stash[j0 + 64 * u] = rk.key_of(sv[u], cv[u], j0 + 64 * u);
       }
       rk.lds = stash;
@@ -504,10 +504,12 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
     int eq_before = 0;
     for (int base = 0; base < n; base += 64 * 8) {
       uint64_t kv[8];
+      if (rk.lds) {   // one test per batch, so the eight reads issue together
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = min(base + 64 * u + lane, n - 1);
-        kv[u] = rk.lds ? rk.lds[j] : rk.compute(j);
+        for (int u = 0; u < 8; ++u) kv[u] = rk.lds[min(base + 64 * u + lane, n - 1)];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kv[u] = rk.compute(min(base + 64 * u + lane, n - 1));
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
