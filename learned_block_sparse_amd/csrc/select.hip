@@ -489,9 +489,10 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
           run += c[q];
         }
       }
-      digit = __shfl(digit, L, 64);
-      above = __shfl(above, L, 64);
-      bucket = __shfl(bucket, L, 64);
+      // L is uniform (from a ballot): scalar lane reads, no LDS round trip
+      digit = __builtin_amdgcn_readlane(digit, L);
+      above = __builtin_amdgcn_readlane(above, L);
+      bucket = __builtin_amdgcn_readlane(bucket, L);
       prefix |= uint64_t(digit) << shift;
       mask |= uint64_t(255) << shift;
       k -= above;
