@@ -20,11 +20,12 @@ namespace veda {
 
 // ------------------------------------------------------------------ pool --
 // One wave per (video tile, q or k, head): 16-byte row reads, LPR lanes per
-// head row, so one load instruction covers RPL rows and the wave keeps all of
-// the tile's rows in flight. Each lane folds its rows into fp64 sums (exact
-// for bf16 and f32 inputs of a tile's range, so the order does not matter)
-// and fp32 max / min; the RPL lane groups are then combined by lane
-// exchanges, and the first group writes the features.
+// head row, so one load instruction covers RPL rows and the unrolled loop
+// keeps several of them in flight. Each lane folds its rows into fp64 sums
+// (exact for bf16 inputs of ordinary range, so the order does not matter;
+// f32 inputs to within fp64 rounding) and fp32 max / min; the RPL lane
+// groups are then combined by lane exchanges, and the first group writes
+// the features.
 template <int D, bool BF16>
 __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a, HeadList heads,
                                                    const int32_t *__restrict__ perm,
