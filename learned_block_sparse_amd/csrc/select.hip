@@ -118,7 +118,8 @@ hipError_t launch_pool(const PoolArgs &a, const HeadList &heads, const int32_t *
 // fp64 GEMM C = A B for the two small products of the predictor (about 4 and
 // 5 GFLOP at 870 video tiles): a 64 x 64 output tile per 256-thread block, K
 // in steps of 16 staged in LDS k-major, each thread a 4 x 4 register tile
-// whose four A and four B values are contiguous (two 16-byte LDS reads each).
+// whose four A values are contiguous and whose four B values are two
+// contiguous pairs (two 16-byte LDS reads each).
 // Two schedules of the same arithmetic: gemm_tile stages one step at a time
 // (68 registers, one 17 KB buffer: seven blocks fit a CU), gemm_tile_pipelined
 // keeps the next step's global reads in flight during the current step's
@@ -132,6 +133,13 @@ constexpr int GT = 64, GK = 16;
 struct GemmTile {
   double acc[4][4];
 };
+
+// Output column of accumulator w of thread column tx: two pairs of adjacent
+// columns 32 apart, so 16 lanes' 16-byte LDS reads of a B row cover 256
+// contiguous bytes, one per bank (four adjacent columns per thread put lanes
+// tx and tx + 8 on the same banks).
+static_assert(GT == 64, "gemm_col covers 64 columns");
+__device__ inline int gemm_col(int tx, int w) { return (w < 2 ? 2 * tx : 32 + 2 * tx - 2) + w; }
 
 // A: [M][K] fp64 row-major. B element (k, n) from load_b(k, n); B_NK says
 // B is stored n-major ([N][K], loaded k-fastest like A) rather than k-major.
@@ -163,8 +171,8 @@ __device__ inline void gemm_tile(const double *A, int M, int K, int i0, int j0, 
     for (int kk = 0; kk < GK; ++kk) {
       const double2 a01 = *reinterpret_cast<const double2 *>(&As[kk][ty * 4]);
       const double2 a23 = *reinterpret_cast<const double2 *>(&As[kk][ty * 4 + 2]);
-      const double2 b01 = *reinterpret_cast<const double2 *>(&Bs[kk][tx * 4]);
-      const double2 b23 = *reinterpret_cast<const double2 *>(&Bs[kk][tx * 4 + 2]);
+      const double2 b01 = *reinterpret_cast<const double2 *>(&Bs[kk][2 * tx]);
+      const double2 b23 = *reinterpret_cast<const double2 *>(&Bs[kk][32 + 2 * tx]);
       const double av[4] = {a01.x, a01.y, a23.x, a23.y};
       const double bv[4] = {b01.x, b01.y, b23.x, b23.y};
 #pragma unroll
@@ -233,8 +241,8 @@ __device__ inline void gemm_tile_pipelined(const double *A, int M, int K, int i0
     for (int kk = 0; kk < GK; ++kk) {
       const double2 a01 = *reinterpret_cast<const double2 *>(&As[buf][kk][ty * 4]);
       const double2 a23 = *reinterpret_cast<const double2 *>(&As[buf][kk][ty * 4 + 2]);
-      const double2 b01 = *reinterpret_cast<const double2 *>(&Bs[buf][kk][tx * 4]);
-      const double2 b23 = *reinterpret_cast<const double2 *>(&Bs[buf][kk][tx * 4 + 2]);
+      const double2 b01 = *reinterpret_cast<const double2 *>(&Bs[buf][kk][2 * tx]);
+      const double2 b23 = *reinterpret_cast<const double2 *>(&Bs[buf][kk][32 + 2 * tx]);
       const double av[4] = {a01.x, a01.y, a23.x, a23.y};
       const double bv[4] = {b01.x, b01.y, b23.x, b23.y};
 #pragma unroll
@@ -272,7 +280,7 @@ __global__ void __launch_bounds__(256) project_kernel(ProjectArgs a) {
     if (i >= nv) continue;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int j = j0 + tx * 4 + w;
+      const int j = j0 + gemm_col(tx, w);
       if (j < D) dst[int64_t(i) * D + j] = t.acc[u][w] + F[int64_t(i) * K + j];
     }
   }
@@ -312,7 +320,7 @@ __global__ void __launch_bounds__(256) score_kernel(ScoreArgs a) {
     if (i >= nv) continue;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int j = j0 + tx * 4 + w;
+      const int j = j0 + gemm_col(tx, w);
       if (j >= nv) continue;
       const double v = t.acc[u][w] / a.sqrt_d;
       C[int64_t(i) * nv + j] = v;
