@@ -78,6 +78,27 @@ def _stream(stream):
     return C.c_void_p(stream.cuda_stream)
 
 
+def _on_callers_stream(fn):
+    """Runs fn with torch's current stream set to its `stream` argument when
+    one is given, so that torch's own work for the call (output and workspace
+    allocations, the projections' index_select, small copies) is ordered with
+    the library's launches on that stream: temporaries are then reused by the
+    caching allocator only after the launches that read them."""
+    import functools
+    import inspect
+    pos = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        stream = kwargs.get("stream") if len(args) <= pos else args[pos]
+        if stream is None:
+            return fn(*args, **kwargs)
+        import torch
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrapped
+
+
 def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
 
@@ -122,6 +143,7 @@ def veda_plan_query(spans, seq_len) -> PlanInfo:
     return info
 
 
+@_on_callers_stream
 def veda_plan(info: PlanInfo, perm=None, valid_count=None, stream=None, device=None):
     """Builds (perm int32 [n_slots], valid_count int32 [n_tiles]) on the device."""
     import torch
@@ -145,6 +167,7 @@ def veda_select_query(info: PlanInfo, generated: Budget, reference: Budget, head
     return sel
 
 
+@_on_callers_stream
 def veda_select(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, heads,
                 proj_q=None, proj_k=None, scores=None, scores_mode=0, row_offsets=None,
                 cols=None, workspace=None, stream=None):
@@ -183,6 +206,7 @@ def veda_select(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, heads,
     return row_offsets, cols
 
 
+@_on_callers_stream
 def veda_select_static(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, heads,
                        proj_q, proj_k, row_offsets=None, cols=None, stream=None):
     """veda_select (scores_mode 0) without a workspace: the library's fixed
@@ -213,6 +237,7 @@ def veda_select_static(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k,
 
 
 # ----------------------------------------------------------------- attend --
+@_on_callers_stream
 def veda_attend(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, v, heads,
                 row_offsets, cols, out=None, scale=0.0, stream=None):
     """Tile-skip attention; writes every row of the listed heads of `out`
@@ -241,6 +266,7 @@ def veda_attend_int8_query(info: PlanInfo, sel: SelectInfo) -> int:
     return int(n.value)
 
 
+@_on_callers_stream
 def veda_attend_int8(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, v, heads,
                      row_offsets, cols, out=None, scale=0.0, workspace=None, stream=None):
     """Tile-skip attention with int8 q.k products (include/veda.h,
@@ -286,6 +312,7 @@ def veda_attend_check(info: PlanInfo, sel: SelectInfo, perm, valid_count, q, k, 
 
 
 # ---------------------------------------------------- teacher and recall --
+@_on_callers_stream
 def veda_teacher(info: PlanInfo, perm, valid_count, q, k, heads, head_dim=None, scale=0.0,
                  teacher=None, stream=None):
     """The max-pooled full-attention teacher map, float32 [n_heads, n_tiles,
@@ -307,6 +334,7 @@ def veda_teacher(info: PlanInfo, perm, valid_count, q, k, heads, head_dim=None, 
     return teacher
 
 
+@_on_callers_stream
 def veda_recall(info: PlanInfo, sel: SelectInfo, row_offsets, cols, teacher, recall=None,
                 stream=None):
     """Per head and query tile, the teacher distribution's share on the tiles
@@ -330,6 +358,7 @@ class Plan:
     valid_count: object
 
 
+@_on_callers_stream
 def plan(spans, seq_len, stream=None, device=None) -> Plan:
     info = veda_plan_query(spans, seq_len)
     perm, vc = veda_plan(info, stream=stream, device=device)
@@ -390,6 +419,7 @@ class Policy:
 _KEEP_ALL = ("ratio", 1.0)
 
 
+@_on_callers_stream
 def attention(q, k, v, refs, target, head_shapes, proj_q, proj_k, generated, reference,
               cache=None, out=None, stats=None, stream=None, fallback=None, layer=None,
               step=None, policy=None, qk="bf16"):

@@ -270,6 +270,38 @@ def test_calls_run_on_the_callers_stream():
     assert torch.equal(got, want)
 
 
+def test_explicit_stream_argument_orders_torch_work():
+    """With stream= given while torch's current stream is another one (the
+    default stream, held busy by a bounded sleep kernel), the call's own torch
+    work (output and workspace allocations, the projections' index_select)
+    goes on the given stream as well: the call completes while the default
+    stream still sleeps, and equals the plain call bit for bit, on the bf16
+    and the int8 path. Projections gathered on the sleeping default stream
+    would reach the selection only after it had read them."""
+    inp, dev, groups = _make("padding")
+    wl = inp.workload
+    args = (wl.refs, wl.target, wl.head_shapes, dev["proj_q"], dev["proj_k"], wl.generated,
+            wl.reference)
+    side = torch.cuda.Stream()
+    for qk in ("bf16", "int8"):
+        want = veda.attention(dev["q"], dev["k"], dev["v"], *args, qk=qk)
+        torch.cuda.synchronize()
+        # freed blocks of the gathered projections' size left holding zeros
+        # in the default stream's pool, where a gather on that stream would
+        # land (zero projections are valid and select other tiles)
+        junk = [torch.zeros((len(g.heads),) + tuple(dev["proj_q"].shape[1:]),
+                            dtype=dev["proj_q"].dtype, device=dev["q"].device)
+                for g in groups for _ in range(2)]
+        del junk
+        torch.cuda._sleep(200_000_000)   # on the default stream
+        got = veda.attention(dev["q"], dev["k"], dev["v"], *args, qk=qk, stream=side)
+        side.synchronize()
+        default_still_busy = not torch.cuda.current_stream().query()
+        torch.cuda.synchronize()
+        assert default_still_busy, "the call waited for the default stream"
+        assert torch.equal(got, want), qk
+
+
 def test_two_streams_at_once_do_not_interfere():
     """Two layers in flight together on two streams (different inputs, each
     with its own workspaces) give what each gives alone, bit for bit: the
