@@ -104,3 +104,50 @@ def test_refusal_from_c_sets_the_error_text(c_program):
                           "budget 0.5 -1 0.5 -1\nhead 1 128\n")
     assert out["plan_status"] == str(_lib.ERR_INVALID)
     assert out["plan_error"]
+
+
+def _build_layer_program(tmp_path):
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc is not available")
+    exe = str(tmp_path / "c_abi_layer")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-isystem", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_abi_layer.c"), "-o", exe, f"-L{libdir}",
+                    "-l:" + os.path.basename(_lib.LIB_PATH), f"-L{os.path.join(ROCM, 'lib')}",
+                    "-lamdhip64", f"-Wl,-rpath,{libdir}"],
+                   check=True, capture_output=True, text=True)
+    return exe
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["padding", "mid"])
+def test_layer_from_a_c_program_matches_the_binding(tmp_path, name):
+    """A C program that allocates its own device buffers and calls veda_plan,
+    veda_select and veda_attend (tests/c_abi_layer.c) writes the same output,
+    bit for bit, as the Python binding's one-call layer on the same inputs."""
+    import numpy as np
+    import torch
+    exe = _build_layer_program(tmp_path)
+    wl = workloads.get(name)
+    assert wl.dtype == "bf16" and set(wl.head_shapes) == {None} and not wl.refs
+    inp = workloads.generate(wl)
+    for n in "qkv":
+        workloads.bf16_bits(getattr(inp, n)).tofile(tmp_path / f"{n}.bin")
+    np.ascontiguousarray(inp.proj_q, dtype=np.float32).tofile(tmp_path / "pq.bin")
+    np.ascontiguousarray(inp.proj_k, dtype=np.float32).tofile(tmp_path / "pk.bin")
+    (tmp_path / "layer.txt").write_text(_spec(wl, None, wl.n_heads))
+    print(f"[c-abi] {name}: running the C program", flush=True)
+    r = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    got = np.fromfile(tmp_path / "out.bin", dtype=np.uint16).reshape(wl.seq_len, wl.n_heads,
+                                                                        wl.head_dim)
+    dev = {n: torch.from_numpy(workloads.bf16_bits(getattr(inp, n)).view(np.int16))
+           .view(torch.bfloat16).cuda() for n in "qkv"}
+    want = veda.attention(dev["q"], dev["k"], dev["v"], wl.refs, wl.target, wl.head_shapes,
+                          torch.from_numpy(inp.proj_q).cuda(), torch.from_numpy(inp.proj_k).cuda(),
+                          wl.generated, wl.reference)
+    torch.cuda.synchronize()
+    want = want.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
