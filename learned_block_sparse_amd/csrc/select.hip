@@ -337,7 +337,8 @@ hipError_t launch_scores(const ScoreArgs &a, hipStream_t s) {
 
 // ---------------------------------------------------------------- select --
 constexpr int SEL_WAVES = 4;
-constexpr int SEL_LDS_KEYS = 2048;   // block widths up to this keep their keys in LDS
+constexpr int SEL_REG_KEYS = 32;                 // keys per lane held in registers
+constexpr int SEL_REG_MAX = 64 * SEL_REG_KEYS;   // block widths up to this keep their keys there
 
 __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -370,7 +371,6 @@ struct RowKeys {
   const double *srow;   // scores of this row, block columns start at srow[start]
   const int32_t *vc;
   int32_t start, own;   // own = column of the row's own tile inside the block, or -1
-  uint64_t *lds;        // NULL when the block is wider than the LDS stash
   __device__ uint64_t key_of(double s, int32_t count, int j) const {
     if (count <= 0) s = -INFINITY;
     if (j == own) s = INFINITY;
@@ -379,11 +379,11 @@ struct RowKeys {
   __device__ uint64_t compute(int j) const { return key_of(srow[start + j], vc[start + j], j); }
 };
 
-// The keys of a wave's row sit in dynamic LDS sized to the widest selecting
-// block of the call (at most SEL_LDS_KEYS per wave; a wider block recomputes
-// its keys on every pass), so narrow layouts fit more workgroups per CU.
-__global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, int32_t stash_keys) {
-  extern __shared__ uint64_t keys_dyn[];
+// A wave's row keeps its keys in registers, key j of the block in slot j / 64
+// of lane j % 64, so every pass reads them without memory traffic and the
+// workgroup needs LDS only for its histograms; a block wider than
+// SEL_REG_MAX recomputes its keys on every pass.
+__global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
   __shared__ int32_t hist_lds[SEL_WAVES][256];
   const int wave = threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
@@ -412,8 +412,8 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
     emit_all(0, a.n_tiles);
     return;
   }
-  uint64_t *stash = keys_dyn + int64_t(wave) * stash_keys;
   int32_t *hist = hist_lds[wave];
+  uint64_t kreg[SEL_REG_KEYS];
   for (int b = 0; b < a.n_blocks; ++b) {
     const veda_block blk = a.blocks[b];
     const int32_t n = blk.stop - blk.start;
@@ -428,42 +428,36 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
     rk.vc = a.valid_count;
     rk.start = blk.start;
     rk.own = (r >= blk.start && r < blk.stop) ? int32_t(r - blk.start) : -1;
-    rk.lds = nullptr;
-    if (n <= stash_keys) {
-      // sixteen logits per lane in flight at a time (indices past the block
-      // re-read its last column and are not stored)
-      for (int j0 = lane; j0 < n; j0 += 64 * 16) {
-        double sv[16];
-        int32_t cv[16];
+    const bool in_regs = n <= SEL_REG_MAX;
+    if (in_regs) {
+      // eight logits per lane in flight at a time (slots past the block
+      // re-read its last column; their keys are never used)
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int j = min(j0 + 64 * u, n - 1);
+      for (int u0 = 0; u0 < SEL_REG_KEYS; u0 += 8) {
+        if (64 * u0 >= n) break;
+        double sv[8];
+        int32_t cv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(lane + 64 * (u0 + u), n - 1);
           sv[u] = rk.srow[rk.start + j];
           cv[u] = rk.vc[rk.start + j];
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (j0 + 64 * u < n) stash[j0 + 64 * u] = rk.key_of(sv[u], cv[u], j0 + 64 * u);
+        for (int u = 0; u < 8; ++u) kreg[u0 + u] = rk.key_of(sv[u], cv[u], lane + 64 * (u0 + u));
       }
-      rk.lds = stash;
-      wave_sync();
     }
     // Radix select of the k-th largest key, 8 bits at a time from the top.
     uint64_t prefix = 0, mask = 0;
     for (int shift = 56; shift >= 0; shift -= 8) {
       for (int i = lane; i < 256; i += 64) hist[i] = 0;
       wave_sync();
-      if (rk.lds) {
-        // eight stashed keys per lane read at a time (indices past the block
-        // re-read its last key and are not counted)
-        for (int j0 = lane; j0 < n; j0 += 64 * 8) {
-          uint64_t kv[8];
+      if (in_regs) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) kv[u] = rk.lds[min(j0 + 64 * u, n - 1)];
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (j0 + 64 * u < n && (kv[u] & mask) == prefix)
-              atomicAdd(&hist[(kv[u] >> shift) & 255], 1);
+        for (int u = 0; u < SEL_REG_KEYS; ++u) {
+          if (64 * u >= n) break;
+          if (lane + 64 * u < n && (kreg[u] & mask) == prefix)
+            atomicAdd(&hist[(kreg[u] >> shift) & 255], 1);
         }
       } else {
         for (int j = lane; j < n; j += 64) {
@@ -508,34 +502,36 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
       wave_sync();
       if (bucket == k) break;   // the whole bucket is kept: no finer digit needed
     }
-    // Emit: keys above the prefix, and the first k keys equal to it by column
-    // (eight keys per lane read at a time, as in the histogram passes).
+    // Emit: keys above the prefix, and the first k keys equal to it by column,
+    // in column order (slot by slot, lanes in order within a slot).
     const uint64_t neg_inf = order_key(-INFINITY);
     int eq_before = 0;
-    for (int base = 0; base < n; base += 64 * 8) {
-      uint64_t kv[8];
-      if (rk.lds) {   // one test per batch, so the eight reads issue together
+    auto emit_key = [&](int j, uint64_t key) {
+      const bool valid = j < n;
+      const uint64_t mk = key & mask;
+      const bool gt = valid && mk > prefix;
+      const bool eq = valid && mk == prefix;
+      const uint64_t eqm = __ballot(eq);
+      const int eqrank = eq_before + __popcll(eqm & lt_mask);
+      const bool keep = (gt || (eq && eqrank < k)) && key != neg_inf;
+      const uint64_t km = __ballot(keep);
+      if (keep) out[pos + __popcll(km & lt_mask)] = blk.start + j;
+      pos += __popcll(km);
+      eq_before += __popcll(eqm);
+    };
+    if (in_regs) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) kv[u] = rk.lds[min(base + 64 * u + lane, n - 1)];
-      } else {
+      for (int u = 0; u < SEL_REG_KEYS; ++u) {
+        if (64 * u >= n) break;
+        emit_key(lane + 64 * u, kreg[u]);
+      }
+    } else {
+      for (int base = 0; base < n; base += 64 * 8) {
+        uint64_t kv[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) kv[u] = rk.compute(min(base + 64 * u + lane, n - 1));
-      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = base + 64 * u + lane;
-        const bool valid = j < n;
-        const uint64_t key = kv[u];
-        const uint64_t mk = key & mask;
-        const bool gt = valid && mk > prefix;
-        const bool eq = valid && mk == prefix;
-        const uint64_t eqm = __ballot(eq);
-        const int eqrank = eq_before + __popcll(eqm & lt_mask);
-        const bool keep = (gt || (eq && eqrank < k)) && key != neg_inf;
-        const uint64_t km = __ballot(keep);
-        if (keep) out[pos + __popcll(km & lt_mask)] = blk.start + j;
-        pos += __popcll(km);
-        eq_before += __popcll(eqm);
+        for (int u = 0; u < 8; ++u) emit_key(base + 64 * u + lane, kv[u]);
       }
     }
     wave_sync();
@@ -545,12 +541,7 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a, in
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   dim3 grid((a.n_tiles + SEL_WAVES - 1) / SEL_WAVES, a.n_heads);
-  int32_t widest = 0;
-  for (int b = 0; b < a.n_blocks; ++b)
-    if (!a.blocks[b].keep_all) widest = max(widest, a.blocks[b].stop - a.blocks[b].start);
-  const int32_t stash = min(widest, SEL_LDS_KEYS);
-  const size_t lds = size_t(SEL_WAVES) * size_t(stash) * sizeof(uint64_t);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(64 * SEL_WAVES), lds, s, a, stash);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(64 * SEL_WAVES), 0, s, a);
   return hipGetLastError();
 }
 
