@@ -337,8 +337,7 @@ hipError_t launch_scores(const ScoreArgs &a, hipStream_t s) {
 
 // ---------------------------------------------------------------- select --
 constexpr int SEL_WAVES = 4;
-constexpr int SEL_REG_KEYS = 32;                 // keys per lane held in registers
-constexpr int SEL_REG_MAX = 64 * SEL_REG_KEYS;   // block widths up to this keep their keys there
+constexpr int SEL_REG_KEYS = 32;                 // most keys per lane held in registers
 
 __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -381,8 +380,11 @@ struct RowKeys {
 
 // A wave's row keeps its keys in registers, key j of the block in slot j / 64
 // of lane j % 64, so every pass reads them without memory traffic and the
-// workgroup needs LDS only for its histograms; a block wider than
-// SEL_REG_MAX recomputes its keys on every pass.
+// workgroup needs LDS only for its histograms. SLOTS (8, 16 or 32 keys per
+// lane) is sized to the call's widest selecting block, so narrow layouts hold
+// fewer registers and fit more waves; a block wider than 64 SLOTS recomputes
+// its keys on every pass.
+template <int SLOTS>
 __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
   __shared__ int32_t hist_lds[SEL_WAVES][256];
   const int wave = threadIdx.x / 64;
@@ -413,7 +415,7 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
     return;
   }
   int32_t *hist = hist_lds[wave];
-  uint64_t kreg[SEL_REG_KEYS];
+  uint64_t kreg[SLOTS];
   for (int b = 0; b < a.n_blocks; ++b) {
     const veda_block blk = a.blocks[b];
     const int32_t n = blk.stop - blk.start;
@@ -428,12 +430,12 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
     rk.vc = a.valid_count;
     rk.start = blk.start;
     rk.own = (r >= blk.start && r < blk.stop) ? int32_t(r - blk.start) : -1;
-    const bool in_regs = n <= SEL_REG_MAX;
+    const bool in_regs = n <= 64 * SLOTS;
     if (in_regs) {
       // eight logits per lane in flight at a time (slots past the block
       // re-read its last column; their keys are never used)
 #pragma unroll
-      for (int u0 = 0; u0 < SEL_REG_KEYS; u0 += 8) {
+      for (int u0 = 0; u0 < SLOTS; u0 += 8) {
         if (64 * u0 >= n) break;
         double sv[8];
         int32_t cv[8];
@@ -454,7 +456,7 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
       wave_sync();
       if (in_regs) {
 #pragma unroll
-        for (int u = 0; u < SEL_REG_KEYS; ++u) {
+        for (int u = 0; u < SLOTS; ++u) {
           if (64 * u >= n) break;
           if (lane + 64 * u < n && (kreg[u] & mask) == prefix)
             atomicAdd(&hist[(kreg[u] >> shift) & 255], 1);
@@ -521,7 +523,7 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
     };
     if (in_regs) {
 #pragma unroll
-      for (int u = 0; u < SEL_REG_KEYS; ++u) {
+      for (int u = 0; u < SLOTS; ++u) {
         if (64 * u >= n) break;
         emit_key(lane + 64 * u, kreg[u]);
       }
@@ -541,7 +543,15 @@ __global__ void __launch_bounds__(64 * SEL_WAVES) select_kernel(SelectArgs a) {
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   dim3 grid((a.n_tiles + SEL_WAVES - 1) / SEL_WAVES, a.n_heads);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(64 * SEL_WAVES), 0, s, a);
+  int32_t widest = 0;
+  for (int b = 0; b < a.n_blocks; ++b)
+    if (!a.blocks[b].keep_all) widest = max(widest, a.blocks[b].stop - a.blocks[b].start);
+  if (widest <= 64 * 8)
+    hipLaunchKernelGGL(select_kernel<8>, grid, dim3(64 * SEL_WAVES), 0, s, a);
+  else if (widest <= 64 * 16)
+    hipLaunchKernelGGL(select_kernel<16>, grid, dim3(64 * SEL_WAVES), 0, s, a);
+  else
+    hipLaunchKernelGGL(select_kernel<SEL_REG_KEYS>, grid, dim3(64 * SEL_WAVES), 0, s, a);
   return hipGetLastError();
 }
 
